@@ -1,0 +1,291 @@
+/*
+ * radix_attn.h — C ABI of the radix-shared KV attention library (MI355X / gfx950).
+ *
+ * What it computes. Requests share K/V through a radix tree of token
+ * sequences: every edge holds a run of tokens plus the K/V slots of those
+ * tokens, lookups match token by token and split an edge where requests
+ * diverge, running requests pin their path with reference counts, and the
+ * least recently used unpinned leaves are evicted first when the one slot
+ * pool shared by cache and running requests runs short
+ * (page "49 · RadixAttention, eviction và cache churn", §2 and §4; SGLang
+ * overview, "SGLang: Mô Hình Lập Trình và Phương Pháp", RadixAttention).
+ * Attention reads each request's keys through its per-request slot list
+ * (req_to_token), both for extend (all new prompt tokens at once against
+ * the cached prefix) and for decode (one new token per request per step)
+ * (AWS blog "Improve performance of Falcon models with Amazon SageMaker",
+ * sections on the KV cache and on batching).
+ *
+ * Conventions for every call:
+ *  - No exception or abort crosses this ABI. Every call that can fail returns
+ *    a radix_status; radix_last_error() gives a thread-local message.
+ *  - RADIX_E_INVAL: a bad argument; nothing launched and no state changed.
+ *  - RADIX_E_NOMEM: not enough free + evictable slots; no state changed.
+ *  - Host objects (pool, tree) are owned by the library (create/destroy) and
+ *    are thread-compatible: one thread at a time per object.
+ *  - Device buffers (pools, queries, outputs, slot lists, workspaces) are owned
+ *    by the caller. The library keeps no device pointer past a call and never
+ *    allocates device memory in attention calls. Device work is enqueued on
+ *    the caller's stream and is asynchronous; host calls are synchronous.
+ *  - Slots are int32 indices into the caller's K/V pool rows.
+ */
+#ifndef RADIX_ATTN_H
+#define RADIX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RADIX_OK = 0,
+  RADIX_E_INVAL = 1,
+  RADIX_E_NOMEM = 2,
+  RADIX_E_HIP = 3,
+  RADIX_E_UNSUPPORTED = 4
+} radix_status;
+
+typedef enum {
+  RADIX_F32 = 0,
+  RADIX_BF16 = 1,
+  RADIX_FP8_E4M3 = 2 /* OCP E4M3FN byte, one fp32 scale per token row */
+} radix_dtype;
+
+/* Thread-local text describing the last non-OK status returned on this thread. */
+const char *radix_last_error(void);
+
+/* Library version string. */
+const char *radix_version(void);
+
+/* ======================================================================
+ * Slot pool (host). One pool serves cached and running requests alike
+ * (page 4 §4). The free list is FIFO and starts as 0..num_slots-1.
+ * ====================================================================== */
+typedef struct radix_kv_pool radix_kv_pool;
+
+/* num_slots >= 0. *out receives the new pool. */
+radix_status radix_kv_pool_create(int64_t num_slots, radix_kv_pool **out);
+void radix_kv_pool_destroy(radix_kv_pool *pool);
+/* Take n slots from the head of the free list into out_slots[n]. All or nothing:
+ * RADIX_E_NOMEM if fewer than n are free. */
+radix_status radix_kv_pool_alloc(radix_kv_pool *pool, int64_t n, int32_t *out_slots);
+/* Append slots[n] to the tail of the free list in the given order. RADIX_E_INVAL
+ * (nothing freed) on an index out of range, a slot already free, or a repeat. */
+radix_status radix_kv_pool_free(radix_kv_pool *pool, const int32_t *slots, int64_t n);
+int64_t radix_kv_pool_num_free(const radix_kv_pool *pool);
+int64_t radix_kv_pool_num_slots(const radix_kv_pool *pool);
+/* Copy the free list, head first, into out[cap]; *n receives its length.
+ * RADIX_E_INVAL if cap is too small (nothing copied, *n still set). */
+radix_status radix_kv_pool_free_list(const radix_kv_pool *pool, int32_t *out, int64_t cap,
+                                     int64_t *n);
+
+/* ======================================================================
+ * Radix tree over int32 token ids (host) — page 4 §2, §4, §5.
+ * A node handle (radix_node) stays valid while the node is pinned.
+ * The tree keeps a logical clock that advances once per match and insert;
+ * least recently used means smallest clock value, ties broken by the
+ * lexicographically smaller root-to-node token path.
+ * ====================================================================== */
+typedef struct radix_tree radix_tree;
+typedef int64_t radix_node; /* 0 = root */
+
+/* The tree draws slots from (and returns them to) `pool`, which must outlive it. */
+radix_status radix_tree_create(radix_kv_pool *pool, radix_tree **out);
+/* Destroys the tree and returns every cached slot to the pool. */
+void radix_tree_destroy(radix_tree *tree);
+
+/* Length of the longest cached prefix of tok[n]; changes nothing (the match may end
+ * inside an edge). Used for longest-prefix-first ordering. */
+radix_status radix_tree_peek(const radix_tree *tree, const int32_t *tok, int64_t n,
+                             int64_t *matched);
+/* Longest cached prefix of tok[n], walking token by token; an edge matched only
+ * partly is split so the match ends on a node. Refreshes the clock of every node on
+ * the matched path. out_slots[n] receives the *matched slots; *last the deepest
+ * matched node (root if none). */
+radix_status radix_tree_match(radix_tree *tree, const int32_t *tok, int64_t n, int64_t *matched,
+                              int32_t *out_slots, radix_node *last);
+/* Pin (+1) / unpin (-1) a node and all its ancestors. Pinned nodes are never evicted.
+ * RADIX_E_INVAL on a stale handle or an unpin below zero. */
+radix_status radix_tree_lock(radix_tree *tree, radix_node node);
+radix_status radix_tree_unlock(radix_tree *tree, radix_node node);
+/* Take n slots from the pool, evicting unpinned leaves least recently used first
+ * (whole nodes; a node whose children are all gone becomes a candidate) until enough
+ * are free. All or nothing: RADIX_E_NOMEM if free + evictable < n. */
+radix_status radix_tree_alloc(radix_tree *tree, int64_t n, int32_t *out_slots);
+/* Insert a finished sequence tok[n] whose K/V live in slots[n] (page 4 §2: the whole
+ * path, outputs included, stays). Tokens already cached keep the tree's slots;
+ * *already_cached receives how many leading tokens were cached before the call. The
+ * tree adopts slots[*already_cached:n]; the caller still owns the rest. */
+radix_status radix_tree_insert(radix_tree *tree, const int32_t *tok, const int32_t *slots,
+                               int64_t n, int64_t *already_cached);
+/* Evict unpinned leaves (LRU first) until at least n_tokens slots are freed or
+ * nothing is evictable; *freed receives the count. */
+radix_status radix_tree_evict(radix_tree *tree, int64_t n_tokens, int64_t *freed);
+
+typedef struct {
+  int64_t cached_tokens;
+  int64_t evictable_tokens;
+  int64_t num_nodes; /* excluding the root */
+  int64_t evicted_tokens_total;
+  int64_t tick;
+} radix_tree_stats;
+radix_status radix_tree_stats_get(const radix_tree *tree, radix_tree_stats *out);
+
+/* Admission order of n waiting requests (page 4 §5). policy 0 = first come first
+ * served; 1 = longest cached prefix first (peek lengths, stable: ties keep arrival
+ * order). tok[i] points at request i's tokens, len[i] their count; out_order[n]
+ * receives request indices. */
+radix_status radix_sched_order(const radix_tree *tree, const int32_t *const *tok,
+                               const int64_t *len, int64_t n, int32_t policy,
+                               int64_t *out_order);
+
+/* Request lifecycle (page 4 §2, §4).
+ * admit: match tok[n], pin the matched path, take n - matched new slots (evicting
+ *        as needed). out_row[n] receives the slot of every prompt position
+ *        (cached then new); *prefix_len the matched length; *node the pinned
+ *        node. On RADIX_E_NOMEM the pin is released, *prefix_len is still set and
+ *        the request stays waiting (the match's splits and clock refresh remain).
+ * finish: insert tok[n] (prompt + generated tokens) with row[n]; give back to the
+ *        pool the slots row[prefix_len:already_cached] that duplicate tokens
+ *        another request cached meanwhile; unpin `node`. */
+radix_status radix_req_admit(radix_tree *tree, const int32_t *tok, int64_t n, int32_t *out_row,
+                             int64_t *prefix_len, radix_node *node);
+radix_status radix_req_finish(radix_tree *tree, const int32_t *tok, const int32_t *row, int64_t n,
+                              int64_t prefix_len, radix_node node, int64_t *already_cached);
+
+/* ======================================================================
+ * Decode plan from the tree: shared segments.
+ * Requests running on one tree node read the same slots for that node's
+ * tokens. A segment is a chain of tree nodes with the same set of at least
+ * `min_members` running requests below it; its keys are read once for all of
+ * them (the one-KV-read-many-query-heads idea of the SGLang feature article,
+ * §一, applied to the requests sharing a radix-tree path). The rest of each
+ * request's keys (positions from req_private_start on) is private.
+ *
+ * nodes[batch]: each request's admission node (pinned). Outputs (host arrays,
+ * capacities in brackets):
+ *   seg_row[cap_seg]      a member (batch index) whose slot list holds the segment
+ *   seg_start/seg_end     key positions [start, end) of the segment
+ *   seg_member_off[cap_seg+1], seg_members[cap_mem], seg_member_slot[cap_mem]
+ *                         CSR of members; seg_member_slot = the segment's rank
+ *                         on that member's path (0 = nearest the root)
+ *   req_num_shared[batch], req_private_start[batch]
+ *   *num_segments, *num_member_entries, *max_members, *max_shared
+ * RADIX_E_INVAL if a capacity is too small (the needed counts are still written
+ * to *num_segments and *num_member_entries). cap_seg >= 2*batch and
+ * cap_mem >= batch*max-path-segments always suffice.
+ * ====================================================================== */
+radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *nodes,
+                                    int32_t batch, int32_t min_members, int32_t cap_seg,
+                                    int32_t cap_mem, int32_t *seg_row, int32_t *seg_start,
+                                    int32_t *seg_end, int32_t *seg_member_off,
+                                    int32_t *seg_members, int32_t *seg_member_slot,
+                                    int32_t *req_num_shared, int32_t *req_private_start,
+                                    int32_t *num_segments, int32_t *num_member_entries,
+                                    int32_t *max_members, int32_t *max_shared);
+
+/* ======================================================================
+ * Device side (HIP, gfx950). All pointers below marked "dev" are device
+ * pointers; everything is enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream).
+ * ====================================================================== */
+typedef struct {
+  int32_t num_q_heads;   /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim_qk;   /* Dqk */
+  int32_t head_dim_v;    /* Dv */
+  int32_t q_dtype;       /* radix_dtype: F32 | BF16; also the output dtype */
+  int32_t kv_dtype;      /* radix_dtype: F32 | BF16 | FP8_E4M3 */
+  int32_t v_is_k_prefix; /* 1: V is the first Dv dims of the K row (MLA; v_pool unused) */
+  float sm_scale;        /* score = sm_scale * <q, k> */
+} radix_attn_shape;
+
+typedef struct {
+  void *k_pool;    /* dev [num_slots, Hkv, Dqk] in kv_dtype */
+  void *v_pool;    /* dev [num_slots, Hkv, Dv] in kv_dtype; NULL when v_is_k_prefix */
+  float *kv_scale; /* dev [num_slots] per-token scale, FP8 only; else NULL */
+  int64_t num_slots;
+} radix_kv_buffers;
+
+/* Shared-segment plan on the device (the arrays of radix_tree_decode_plan). */
+typedef struct {
+  int32_t num_segments;
+  int32_t num_member_entries;                   /* length of seg_members */
+  const int32_t *seg_row, *seg_start, *seg_end; /* dev [num_segments] */
+  const int32_t *seg_member_off;                /* dev [num_segments + 1] */
+  const int32_t *seg_members, *seg_member_slot; /* dev [num_member_entries] */
+  const int32_t *req_num_shared;                /* dev [batch] */
+  const int32_t *req_private_start;             /* dev [batch] */
+  int32_t max_members;                          /* host: largest member count */
+  int32_t max_shared;                           /* host: largest req_num_shared */
+  int32_t max_seg_len;                          /* host: longest segment in tokens */
+} radix_decode_plan;
+
+/* Shapes compiled into this library (anything else: RADIX_E_UNSUPPORTED):
+ *   q F32, kv F32,  Dqk = Dv = 64,   Hq/Hkv in {1, 2, 4, 8}      (extend, decode)
+ *   q BF16, kv BF16, Dqk = Dv = 128, Hq/Hkv in {1, 2, 4, 8}      (extend, decode)
+ *   q BF16, kv BF16 or FP8_E4M3, Dqk = 576, Dv = 512, Hkv = 1,
+ *       Hq = 128, v_is_k_prefix = 1                              (decode, store)  */
+radix_status radix_attn_supported(const radix_attn_shape *shape, int is_decode);
+
+/* Store K/V rows (one per token, all KV heads) at their slots:
+ * k_pool[slots[t]] = k_new[t], v_pool[slots[t]] = v_new[t], kv_scale[slots[t]] = scale_new[t].
+ * k_new dev [T, Hkv, Dqk], v_new dev [T, Hkv, Dv] (ignored when v_is_k_prefix),
+ * scale_new dev [T] (FP8 only). Slots must be distinct and < num_slots. */
+radix_status radix_kv_store(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                            const void *k_new, const void *v_new, const float *scale_new,
+                            const int32_t *slots, int64_t num_tokens, void *stream);
+
+/* Workspace bytes radix_attn_decode needs for `batch` requests of at most
+ * `max_seq_len` tokens, at most `max_shared` shared segments each and `num_splits`
+ * private splits (0 = the split count radix_attn_decode chooses itself). */
+radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int32_t batch,
+                                              int32_t max_seq_len, int32_t max_shared,
+                                              int32_t num_splits, size_t *bytes);
+
+/* Extend attention (prefill of new tokens against each request's cached prefix).
+ * Request b (rows req_rows[b] of req_to_token, or b when req_rows is NULL) has
+ * prefix_lens[b] cached tokens and extend_lens[b] new ones; its new tokens are
+ * rows cu_extend[b] .. cu_extend[b+1]-1 of q/k_new/v_new/out. New token i sits
+ * at position prefix_lens[b] + i and attends keys 0 .. prefix_lens[b] + i
+ * (causal, itself included), all read through req_to_token[row][pos]: the
+ * caller has already written the new tokens' slots into the rows.
+ * When k_new is not NULL the new rows are first stored at those slots.
+ *   q dev [T, Hq, Dqk] (q_dtype), out dev [T, Hq, Dv] (q_dtype), lse_out dev [T, Hq]
+ *   fp32 natural-log log-sum-exp of the scaled scores, or NULL.
+ *   req_to_token dev [rows, rtt_stride] int32; prefix_lens, extend_lens dev [batch];
+ *   cu_extend dev [batch+1]. Host scalars: total_extend = T, max_extend = max
+ *   extend_lens (grid sizing); values above it are an error of the caller. */
+radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                               const void *q, const void *k_new, const void *v_new,
+                               const float *scale_new, const int32_t *req_to_token,
+                               int32_t rtt_stride, const int32_t *req_rows,
+                               const int32_t *prefix_lens, const int32_t *extend_lens,
+                               const int32_t *cu_extend, int32_t batch, int32_t total_extend,
+                               int32_t max_extend, void *out, float *lse_out, void *stream);
+
+/* Decode attention: request b's query (position seq_lens[b]-1) attends keys
+ * 0 .. seq_lens[b]-1 read through req_to_token[row]. When new_slots is not NULL,
+ * first req_to_token[row][seq_lens[b]-1] = new_slots[b] and the new K/V row
+ * (k_new/v_new/scale_new dev [batch, Hkv, *]) is stored at that slot.
+ * With a plan, each shared segment's keys are read once for all its members and
+ * keys from req_private_start[b] on are read per request, split into
+ * `num_splits` chunks (0 = choose); all partial results are merged exactly by
+ * their log-sum-exp. Without a plan (NULL) every request reads all its keys.
+ *   q dev [batch, Hq, Dqk]; out dev [batch, Hq, Dv]; lse_out dev [batch, Hq] or NULL;
+ *   workspace dev, at least radix_attn_decode_workspace_size bytes.
+ *   max_seq_len: host bound on seq_lens (grid sizing). */
+radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                               const void *q, const void *k_new, const void *v_new,
+                               const float *scale_new, const int32_t *new_slots,
+                               int32_t *req_to_token, int32_t rtt_stride,
+                               const int32_t *req_rows, const int32_t *seq_lens, int32_t batch,
+                               int32_t max_seq_len, const radix_decode_plan *plan,
+                               int32_t num_splits, void *out, float *lse_out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RADIX_ATTN_H */

@@ -1,0 +1,382 @@
+"""ctypes binding of libradix_attn.so (argument marshalling only).
+
+Every step of the path runs in the native library: the host tree, pool and
+scheduler in C++, the attention in HIP kernels. This module only converts
+numpy arrays / torch tensors to pointers and status codes to exceptions. It
+raises if the library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libradix_attn.so")
+
+OK, E_INVAL, E_NOMEM, E_HIP, E_UNSUPPORTED = 0, 1, 2, 3, 4
+F32, BF16, FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+
+_i32p = C.POINTER(C.c_int32)
+_i64p = C.POINTER(C.c_int64)
+_vp = C.c_void_p
+
+
+class RadixError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"radix status {status}: {msg}")
+        self.status = status
+
+
+class NoMemory(RadixError):
+    pass
+
+
+class TreeStats(C.Structure):
+    _fields_ = [("cached_tokens", C.c_int64), ("evictable_tokens", C.c_int64),
+                ("num_nodes", C.c_int64), ("evicted_tokens_total", C.c_int64), ("tick", C.c_int64)]
+
+
+class AttnShape(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim_qk", C.c_int32),
+                ("head_dim_v", C.c_int32), ("q_dtype", C.c_int32), ("kv_dtype", C.c_int32),
+                ("v_is_k_prefix", C.c_int32), ("sm_scale", C.c_float)]
+
+
+class KVBuffers(C.Structure):
+    _fields_ = [("k_pool", _vp), ("v_pool", _vp), ("kv_scale", _vp), ("num_slots", C.c_int64)]
+
+
+class DecodePlan(C.Structure):
+    _fields_ = [("num_segments", C.c_int32), ("num_member_entries", C.c_int32),
+                ("seg_row", _vp), ("seg_start", _vp), ("seg_end", _vp), ("seg_member_off", _vp),
+                ("seg_members", _vp), ("seg_member_slot", _vp), ("req_num_shared", _vp),
+                ("req_private_start", _vp), ("max_members", C.c_int32), ("max_shared", C.c_int32),
+                ("max_seg_len", C.c_int32)]
+
+
+_SIGS = {
+    "radix_last_error": (C.c_char_p, []),
+    "radix_version": (C.c_char_p, []),
+    "radix_kv_pool_create": (C.c_int, [C.c_int64, C.POINTER(_vp)]),
+    "radix_kv_pool_destroy": (None, [_vp]),
+    "radix_kv_pool_alloc": (C.c_int, [_vp, C.c_int64, _i32p]),
+    "radix_kv_pool_free": (C.c_int, [_vp, _i32p, C.c_int64]),
+    "radix_kv_pool_num_free": (C.c_int64, [_vp]),
+    "radix_kv_pool_num_slots": (C.c_int64, [_vp]),
+    "radix_kv_pool_free_list": (C.c_int, [_vp, _i32p, C.c_int64, _i64p]),
+    "radix_tree_create": (C.c_int, [_vp, C.POINTER(_vp)]),
+    "radix_tree_destroy": (None, [_vp]),
+    "radix_tree_peek": (C.c_int, [_vp, _i32p, C.c_int64, _i64p]),
+    "radix_tree_match": (C.c_int, [_vp, _i32p, C.c_int64, _i64p, _i32p, _i64p]),
+    "radix_tree_lock": (C.c_int, [_vp, C.c_int64]),
+    "radix_tree_unlock": (C.c_int, [_vp, C.c_int64]),
+    "radix_tree_alloc": (C.c_int, [_vp, C.c_int64, _i32p]),
+    "radix_tree_insert": (C.c_int, [_vp, _i32p, _i32p, C.c_int64, _i64p]),
+    "radix_tree_evict": (C.c_int, [_vp, C.c_int64, _i64p]),
+    "radix_tree_stats_get": (C.c_int, [_vp, C.POINTER(TreeStats)]),
+    "radix_sched_order": (C.c_int, [_vp, C.POINTER(_i32p), _i64p, C.c_int64, C.c_int32, _i64p]),
+    "radix_req_admit": (C.c_int, [_vp, _i32p, C.c_int64, _i32p, _i64p, _i64p]),
+    "radix_req_finish": (C.c_int, [_vp, _i32p, _i32p, C.c_int64, C.c_int64, C.c_int64, _i64p]),
+    "radix_tree_decode_plan": (C.c_int, [_vp, _i64p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                         _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
+                                         _i32p, _i32p, _i32p, _i32p]),
+    "radix_attn_supported": (C.c_int, [C.POINTER(AttnShape), C.c_int]),
+    "radix_kv_store": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp, _vp, _vp,
+                                 C.c_int64, _vp]),
+    "radix_attn_decode_workspace_size": (C.c_int, [C.POINTER(AttnShape), C.c_int32, C.c_int32,
+                                                   C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]),
+    "radix_attn_extend": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp, _vp, _vp,
+                                    _vp, C.c_int32, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
+                                    C.c_int32, _vp, _vp, _vp]),
+    "radix_attn_decode": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp, _vp, _vp,
+                                    _vp, _vp, C.c_int32, _vp, _vp, C.c_int32, C.c_int32,
+                                    C.POINTER(DecodePlan), C.c_int32, _vp, _vp, _vp, C.c_size_t,
+                                    _vp]),
+}
+
+_LIB = None
+
+
+def load():
+    """Load the built library (raises if it is missing: there is no fallback)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m prefix_shared_kv_radix_amd.build`")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def _check(status):
+    if status != OK:
+        msg = load().radix_last_error().decode(errors="replace")
+        if status == E_NOMEM:
+            raise NoMemory(status, msg)
+        raise RadixError(status, msg)
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_i32p)
+
+
+# ---------------------------------------------------------------------- host
+class KVPool:
+    """Slot pool (host). Owns the native object."""
+
+    def __init__(self, num_slots: int):
+        lib = load()
+        h = _vp()
+        _check(lib.radix_kv_pool_create(int(num_slots), C.byref(h)))
+        self.h = h
+
+    def close(self):
+        if self.h:
+            load().radix_kv_pool_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+    def alloc(self, n: int) -> np.ndarray:
+        out = np.empty(int(n), np.int32)
+        _check(load().radix_kv_pool_alloc(self.h, int(n), out.ctypes.data_as(_i32p)))
+        return out
+
+    def free(self, slots) -> None:
+        a, p = _i32(slots)
+        _check(load().radix_kv_pool_free(self.h, p, len(a)))
+
+    def num_free(self) -> int:
+        return int(load().radix_kv_pool_num_free(self.h))
+
+    def free_list(self) -> np.ndarray:
+        n = C.c_int64()
+        cap = self.num_free()
+        out = np.empty(max(cap, 1), np.int32)
+        _check(load().radix_kv_pool_free_list(self.h, out.ctypes.data_as(_i32p), cap, C.byref(n)))
+        return out[:n.value].copy()
+
+
+class RadixTree:
+    """Radix tree over token ids (host). Keeps its pool alive."""
+
+    def __init__(self, pool: KVPool):
+        lib = load()
+        h = _vp()
+        _check(lib.radix_tree_create(pool.h, C.byref(h)))
+        self.h = h
+        self.pool = pool
+
+    def close(self):
+        if self.h:
+            load().radix_tree_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+    def peek(self, tokens) -> int:
+        a, p = _i32(tokens)
+        m = C.c_int64()
+        _check(load().radix_tree_peek(self.h, p, len(a), C.byref(m)))
+        return m.value
+
+    def match(self, tokens):
+        a, p = _i32(tokens)
+        m, node = C.c_int64(), C.c_int64()
+        out = np.empty(max(len(a), 1), np.int32)
+        _check(load().radix_tree_match(self.h, p, len(a), C.byref(m), out.ctypes.data_as(_i32p),
+                                       C.byref(node)))
+        return m.value, out[:m.value].copy(), node.value
+
+    def lock(self, node):
+        _check(load().radix_tree_lock(self.h, int(node)))
+
+    def unlock(self, node):
+        _check(load().radix_tree_unlock(self.h, int(node)))
+
+    def alloc(self, n: int) -> np.ndarray:
+        out = np.empty(max(int(n), 1), np.int32)
+        _check(load().radix_tree_alloc(self.h, int(n), out.ctypes.data_as(_i32p)))
+        return out[:int(n)]
+
+    def insert(self, tokens, slots) -> int:
+        a, pa = _i32(tokens)
+        b, pb = _i32(slots)
+        if len(a) != len(b):
+            raise ValueError("tokens and slots differ in length")
+        c = C.c_int64()
+        _check(load().radix_tree_insert(self.h, pa, pb, len(a), C.byref(c)))
+        return c.value
+
+    def evict(self, n: int) -> int:
+        f = C.c_int64()
+        _check(load().radix_tree_evict(self.h, int(n), C.byref(f)))
+        return f.value
+
+    def stats(self) -> TreeStats:
+        s = TreeStats()
+        _check(load().radix_tree_stats_get(self.h, C.byref(s)))
+        return s
+
+    def sched_order(self, prompts, policy: str):
+        arrs = [np.ascontiguousarray(p, dtype=np.int32) for p in prompts]
+        n = len(arrs)
+        ptrs = (_i32p * max(n, 1))(*[a.ctypes.data_as(_i32p) for a in arrs])
+        lens = np.array([len(a) for a in arrs], np.int64)
+        out = np.empty(max(n, 1), np.int64)
+        code = {"fcfs": 0, "lpf": 1}[policy]
+        _check(load().radix_sched_order(self.h, ptrs, lens.ctypes.data_as(_i64p), n, code,
+                                        out.ctypes.data_as(_i64p)))
+        return out[:n].tolist()
+
+    def admit(self, tokens):
+        """(prefix_len, row slots, node); raises NoMemory (request stays waiting)."""
+        a, p = _i32(tokens)
+        row = np.empty(max(len(a), 1), np.int32)
+        m, node = C.c_int64(), C.c_int64()
+        st = load().radix_req_admit(self.h, p, len(a), row.ctypes.data_as(_i32p), C.byref(m),
+                                    C.byref(node))
+        _check(st)
+        return m.value, row[:len(a)], node.value
+
+    def finish(self, tokens, row, prefix_len, node) -> int:
+        a, pa = _i32(tokens)
+        b, pb = _i32(row)
+        c = C.c_int64()
+        _check(load().radix_req_finish(self.h, pa, pb, len(a), int(prefix_len), int(node),
+                                       C.byref(c)))
+        return c.value
+
+    def decode_plan(self, nodes, min_members: int = 2):
+        """Shared-segment plan (host arrays) for requests admitted at `nodes`."""
+        nodes = np.ascontiguousarray(nodes, dtype=np.int64)
+        B = len(nodes)
+        cap_seg = max(2 * B, 1)
+        cap_mem = max(B * 8, 1)
+        while True:
+            seg = [np.zeros(cap_seg + (1 if k == 3 else 0), np.int32) for k in range(4)]
+            mem = [np.zeros(cap_mem, np.int32) for _ in range(2)]
+            req = [np.zeros(max(B, 1), np.int32) for _ in range(2)]
+            cnt = [C.c_int32() for _ in range(4)]
+            st = load().radix_tree_decode_plan(
+                self.h, nodes.ctypes.data_as(_i64p), B, int(min_members), cap_seg, cap_mem,
+                *[x.ctypes.data_as(_i32p) for x in seg], *[x.ctypes.data_as(_i32p) for x in mem],
+                *[x.ctypes.data_as(_i32p) for x in req], *[C.byref(c) for c in cnt])
+            ns, nm = cnt[0].value, cnt[1].value
+            if st == E_INVAL and (ns > cap_seg or nm > cap_mem):
+                cap_seg, cap_mem = max(cap_seg, ns), max(cap_mem, nm)
+                continue
+            _check(st)
+            break
+        return HostPlan(seg_row=seg[0][:ns], seg_start=seg[1][:ns], seg_end=seg[2][:ns],
+                        seg_member_off=seg[3][:ns + 1] if ns else np.zeros(1, np.int32),
+                        seg_members=mem[0][:nm], seg_member_slot=mem[1][:nm],
+                        req_num_shared=req[0][:B], req_private_start=req[1][:B],
+                        max_members=cnt[2].value, max_shared=cnt[3].value)
+
+
+@dataclass
+class HostPlan:
+    seg_row: np.ndarray
+    seg_start: np.ndarray
+    seg_end: np.ndarray
+    seg_member_off: np.ndarray
+    seg_members: np.ndarray
+    seg_member_slot: np.ndarray
+    req_num_shared: np.ndarray
+    req_private_start: np.ndarray
+    max_members: int
+    max_shared: int
+
+    @property
+    def num_segments(self):
+        return len(self.seg_row)
+
+    @property
+    def max_seg_len(self):
+        return int((self.seg_end - self.seg_start).max()) if len(self.seg_row) else 0
+
+
+# ---------------------------------------------------------------------- device
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream)
+
+
+def make_shape(num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, q_dtype, kv_dtype,
+               v_is_k_prefix, sm_scale) -> AttnShape:
+    return AttnShape(num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, DTYPE_CODES[q_dtype],
+                     DTYPE_CODES[kv_dtype], int(bool(v_is_k_prefix)), float(sm_scale))
+
+
+def make_kv(k_pool, v_pool, kv_scale) -> KVBuffers:
+    return KVBuffers(_ptr(k_pool), _ptr(v_pool), _ptr(kv_scale), int(k_pool.shape[0]))
+
+
+def attn_supported(shape: AttnShape, is_decode: bool) -> bool:
+    return load().radix_attn_supported(C.byref(shape), int(is_decode)) == OK
+
+
+def kv_store(shape, kv, k_new, v_new, scale_new, slots, stream=None):
+    _check(load().radix_kv_store(C.byref(shape), C.byref(kv), _ptr(k_new), _ptr(v_new),
+                                 _ptr(scale_new), _ptr(slots), int(slots.numel()), _stream(stream)))
+
+
+def decode_workspace_size(shape, batch, max_seq_len, max_shared, num_splits) -> int:
+    n = C.c_size_t()
+    _check(load().radix_attn_decode_workspace_size(C.byref(shape), int(batch), int(max_seq_len),
+                                                   int(max_shared), int(num_splits), C.byref(n)))
+    return n.value
+
+
+def attn_extend(shape, kv, q, k_new, v_new, scale_new, req_to_token, req_rows, prefix_lens,
+                extend_lens, cu_extend, batch, total_extend, max_extend, out, lse_out=None,
+                stream=None):
+    _check(load().radix_attn_extend(
+        C.byref(shape), C.byref(kv), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(scale_new),
+        _ptr(req_to_token), int(req_to_token.shape[1]), _ptr(req_rows), _ptr(prefix_lens),
+        _ptr(extend_lens), _ptr(cu_extend), int(batch), int(total_extend), int(max_extend),
+        _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def device_plan(plan: HostPlan, device):
+    """Upload a HostPlan; returns (DecodePlan struct, tensors kept alive by the caller)."""
+    import torch
+    if plan is None or plan.num_segments == 0:
+        return None, []
+    ts = [torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in
+          (plan.seg_row, plan.seg_start, plan.seg_end, plan.seg_member_off, plan.seg_members,
+           plan.seg_member_slot, plan.req_num_shared, plan.req_private_start)]
+    dp = DecodePlan(plan.num_segments, len(plan.seg_members), *[_vp(t.data_ptr()) for t in ts],
+                    plan.max_members, plan.max_shared, plan.max_seg_len)
+    return dp, ts
+
+
+def attn_decode(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token, req_rows, seq_lens,
+                batch, max_seq_len, plan, num_splits, out, lse_out, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().radix_attn_decode(
+        C.byref(shape), C.byref(kv), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(scale_new),
+        _ptr(new_slots), _ptr(req_to_token), int(req_to_token.shape[1]), _ptr(req_rows),
+        _ptr(seq_lens), int(batch), int(max_seq_len), None if plan is None else C.byref(plan),
+        int(num_splits), _ptr(out), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(stream)))

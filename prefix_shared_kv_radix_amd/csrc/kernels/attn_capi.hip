@@ -1,0 +1,291 @@
+// C entry points of the device path: argument checks on the host, then
+// kernel launches on the caller's stream. Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "attn_args.hpp"
+#include "host/radix_host.hpp"
+#include "radix_attn.h"
+
+using radix::set_error;
+using radix_launch::AttnArgs;
+using radix_launch::StoreArgs;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+#define REQUIRE(cond, msg) \
+  do {                     \
+    if (!(cond)) {         \
+      set_error(msg);      \
+      return RADIX_E_INVAL; \
+    }                      \
+  } while (0)
+
+enum class Kind { None, GqaF32, GqaBf16, MlaBf16, MlaFp8 };
+
+Kind classify(const radix_attn_shape *s) {
+  if (!s || s->num_kv_heads <= 0 || s->num_q_heads <= 0 || s->num_q_heads % s->num_kv_heads)
+    return Kind::None;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
+  if (!s->v_is_k_prefix && g_ok) {
+    if (s->q_dtype == RADIX_F32 && s->kv_dtype == RADIX_F32 && s->head_dim_qk == 64 &&
+        s->head_dim_v == 64)
+      return Kind::GqaF32;
+    if (s->q_dtype == RADIX_BF16 && s->kv_dtype == RADIX_BF16 && s->head_dim_qk == 128 &&
+        s->head_dim_v == 128)
+      return Kind::GqaBf16;
+  }
+  if (s->v_is_k_prefix && s->num_kv_heads == 1 && s->num_q_heads == 128 && s->head_dim_qk == 576 &&
+      s->head_dim_v == 512 && s->q_dtype == RADIX_BF16) {
+    if (s->kv_dtype == RADIX_BF16) return Kind::MlaBf16;
+    if (s->kv_dtype == RADIX_FP8_E4M3) return Kind::MlaFp8;
+  }
+  return Kind::None;
+}
+
+int elem_bytes(int dtype) { return dtype == RADIX_F32 ? 4 : dtype == RADIX_BF16 ? 2 : 1; }
+
+radix_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return RADIX_OK;
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return RADIX_E_HIP;
+}
+
+radix_status check_kv(const radix_attn_shape *s, const radix_kv_buffers *kv) {
+  REQUIRE(kv && kv->k_pool && kv->num_slots > 0, "missing K/V pool");
+  REQUIRE(s->v_is_k_prefix || kv->v_pool, "missing V pool");
+  REQUIRE(s->kv_dtype != RADIX_FP8_E4M3 || kv->kv_scale, "fp8 pool needs per-token scales");
+  return RADIX_OK;
+}
+
+StoreArgs store_args(const radix_attn_shape *s, const radix_kv_buffers *kv, const void *k_new,
+                     const void *v_new, const float *scale_new) {
+  StoreArgs a{};
+  const int eb = elem_bytes(s->kv_dtype);
+  a.k_new = static_cast<const uint8_t *>(k_new);
+  a.v_new = s->v_is_k_prefix ? nullptr : static_cast<const uint8_t *>(v_new);
+  a.scale_new = s->kv_dtype == RADIX_FP8_E4M3 ? scale_new : nullptr;
+  a.k_pool = static_cast<uint8_t *>(kv->k_pool);
+  a.v_pool = static_cast<uint8_t *>(kv->v_pool);
+  a.kv_scale = kv->kv_scale;
+  a.k_row_bytes = s->num_kv_heads * s->head_dim_qk * eb;
+  a.v_row_bytes = s->num_kv_heads * s->head_dim_v * eb;
+  return a;
+}
+
+AttnArgs attn_args(const radix_attn_shape *s, const radix_kv_buffers *kv, const void *q,
+                   const int32_t *rtt, int32_t stride, const int32_t *rows, void *out,
+                   float *lse) {
+  AttnArgs a{};
+  a.q = q;
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.rtt = rtt;
+  a.rtt_stride = stride;
+  a.req_rows = rows;
+  a.out = out;
+  a.lse = lse;
+  a.Hq = s->num_q_heads;
+  a.Hkv = s->num_kv_heads;
+  a.scale_log2 = s->sm_scale * kLog2e;
+  return a;
+}
+
+int auto_splits(int batch, int hkv, int max_seq_len) {
+  const int target = 2048;  // resident blocks to fill 256 CUs several times over
+  int s = (target + batch * hkv - 1) / (batch * hkv > 0 ? batch * hkv : 1);
+  const int cap = max_seq_len / 256 > 1 ? max_seq_len / 256 : 1;
+  if (s > cap) s = cap;
+  if (s > 32) s = 32;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+extern "C" {
+
+radix_status radix_mla_decode_impl(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                                   const void *q, const int32_t *rtt, int32_t stride,
+                                   const int32_t *rows, const int32_t *seq_lens, int32_t batch,
+                                   int32_t max_seq_len, const radix_decode_plan *plan,
+                                   int32_t num_splits, void *out, float *lse, float *ws_o,
+                                   float *ws_lse, int32_t parts, hipStream_t stream);
+
+radix_status radix_attn_supported(const radix_attn_shape *shape, int is_decode) {
+  Kind k = classify(shape);
+  if (k == Kind::None) {
+    set_error("unsupported attention shape/dtype combination");
+    return RADIX_E_UNSUPPORTED;
+  }
+  if (!is_decode && (k == Kind::MlaBf16 || k == Kind::MlaFp8)) {
+    set_error("MLA extend is not part of this library");
+    return RADIX_E_UNSUPPORTED;
+  }
+  return RADIX_OK;
+}
+
+radix_status radix_kv_store(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                            const void *k_new, const void *v_new, const float *scale_new,
+                            const int32_t *slots, int64_t num_tokens, void *stream) {
+  if (radix_attn_supported(shape, 1) != RADIX_OK) return RADIX_E_UNSUPPORTED;
+  radix_status st = check_kv(shape, kv);
+  if (st != RADIX_OK) return st;
+  REQUIRE(num_tokens >= 0 && num_tokens <= 0x7fffffff, "token count out of range");
+  if (num_tokens == 0) return RADIX_OK;
+  REQUIRE(k_new && slots, "missing new rows or slots");
+  REQUIRE(shape->v_is_k_prefix || v_new, "missing new V rows");
+  REQUIRE(shape->kv_dtype != RADIX_FP8_E4M3 || scale_new, "missing new fp8 scales");
+  StoreArgs a = store_args(shape, kv, k_new, v_new, scale_new);
+  a.slots = slots;
+  a.mode = 0;
+  return hip_status(radix_launch::kv_store(a, num_tokens, static_cast<hipStream_t>(stream)),
+                    "kv_store launch");
+}
+
+radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int32_t batch,
+                                              int32_t max_seq_len, int32_t max_shared,
+                                              int32_t num_splits, size_t *bytes) {
+  REQUIRE(shape && bytes && batch >= 0 && max_seq_len >= 0 && max_shared >= 0 && num_splits >= 0,
+          "bad workspace query");
+  if (num_splits == 0) num_splits = auto_splits(batch, shape->num_kv_heads, max_seq_len);
+  const size_t parts = static_cast<size_t>(max_shared) + static_cast<size_t>(num_splits);
+  *bytes = static_cast<size_t>(batch) * shape->num_q_heads * parts *
+           (static_cast<size_t>(shape->head_dim_v) + 1) * sizeof(float);
+  return RADIX_OK;
+}
+
+radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                               const void *q, const void *k_new, const void *v_new,
+                               const float *scale_new, const int32_t *req_to_token,
+                               int32_t rtt_stride, const int32_t *req_rows,
+                               const int32_t *prefix_lens, const int32_t *extend_lens,
+                               const int32_t *cu_extend, int32_t batch, int32_t total_extend,
+                               int32_t max_extend, void *out, float *lse_out, void *stream) {
+  if (radix_attn_supported(shape, 0) != RADIX_OK) return RADIX_E_UNSUPPORTED;
+  radix_status st = check_kv(shape, kv);
+  if (st != RADIX_OK) return st;
+  REQUIRE(batch >= 0 && total_extend >= 0 && max_extend >= 0, "negative sizes");
+  if (batch == 0 || total_extend == 0) return RADIX_OK;
+  REQUIRE(q && out && req_to_token && rtt_stride > 0 && prefix_lens && extend_lens && cu_extend,
+          "missing extend argument");
+  REQUIRE(max_extend <= total_extend, "max_extend exceeds total_extend");
+  REQUIRE(!k_new || shape->v_is_k_prefix || v_new, "missing new V rows");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k_new) {
+    StoreArgs sa = store_args(shape, kv, k_new, v_new, scale_new);
+    sa.rtt = const_cast<int32_t *>(req_to_token);
+    sa.rtt_stride = rtt_stride;
+    sa.req_rows = req_rows;
+    sa.prefix_lens = prefix_lens;
+    sa.cu_extend = cu_extend;
+    sa.batch = batch;
+    sa.mode = 2;
+    st = hip_status(radix_launch::kv_store(sa, total_extend, s), "kv_store launch");
+    if (st != RADIX_OK) return st;
+  }
+  AttnArgs a = attn_args(shape, kv, q, req_to_token, rtt_stride, req_rows, out, lse_out);
+  a.prefix_lens = prefix_lens;
+  a.extend_lens = extend_lens;
+  a.cu_extend = cu_extend;
+  a.batch = batch;
+  a.num_splits = 1;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (classify(shape) == Kind::GqaBf16)
+    return hip_status(radix_launch::mfma(G, false, a, max_extend * G, batch, s), "extend launch");
+  return hip_status(radix_launch::valu(false, G, 1, a, total_extend, 1, s), "extend launch");
+}
+
+radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                               const void *q, const void *k_new, const void *v_new,
+                               const float *scale_new, const int32_t *new_slots,
+                               int32_t *req_to_token, int32_t rtt_stride,
+                               const int32_t *req_rows, const int32_t *seq_lens, int32_t batch,
+                               int32_t max_seq_len, const radix_decode_plan *plan,
+                               int32_t num_splits, void *out, float *lse_out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (radix_attn_supported(shape, 1) != RADIX_OK) return RADIX_E_UNSUPPORTED;
+  radix_status st = check_kv(shape, kv);
+  if (st != RADIX_OK) return st;
+  REQUIRE(batch >= 0 && max_seq_len >= 0 && num_splits >= 0, "negative sizes");
+  if (batch == 0) return RADIX_OK;
+  REQUIRE(q && out && req_to_token && rtt_stride > 0 && seq_lens, "missing decode argument");
+  REQUIRE(max_seq_len >= 1 && max_seq_len <= rtt_stride, "max_seq_len outside [1, rtt_stride]");
+  REQUIRE(!k_new || shape->v_is_k_prefix || v_new, "missing new V rows");
+  REQUIRE(!k_new || shape->kv_dtype != RADIX_FP8_E4M3 || scale_new, "missing new fp8 scales");
+  const bool use_plan = plan && plan->num_segments > 0;
+  if (use_plan) {
+    REQUIRE(plan->seg_row && plan->seg_start && plan->seg_end && plan->seg_member_off &&
+                plan->seg_members && plan->seg_member_slot && plan->req_num_shared &&
+                plan->req_private_start && plan->num_member_entries > 0 &&
+                plan->max_members > 0 && plan->max_shared > 0,
+            "incomplete decode plan");
+  }
+  const int splits = num_splits > 0 ? num_splits
+                                    : auto_splits(batch, shape->num_kv_heads, max_seq_len);
+  const int max_shared = use_plan ? plan->max_shared : 0;
+  const int parts = max_shared + splits;
+  const bool direct = !use_plan && splits == 1;
+  size_t need = 0;
+  radix_attn_decode_workspace_size(shape, batch, max_seq_len, max_shared, splits, &need);
+  REQUIRE(direct || (workspace && workspace_bytes >= need), "decode workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (k_new) {
+    StoreArgs sa = store_args(shape, kv, k_new, v_new, scale_new);
+    sa.new_slots = new_slots;
+    sa.rtt = req_to_token;
+    sa.rtt_stride = rtt_stride;
+    sa.req_rows = req_rows;
+    sa.seq_lens = seq_lens;
+    sa.mode = new_slots ? 1 : 3;
+    st = hip_status(radix_launch::kv_store(sa, batch, s), "kv_store launch");
+    if (st != RADIX_OK) return st;
+  }
+
+  float *ws_o = direct ? nullptr : static_cast<float *>(workspace);
+  float *ws_lse = direct ? nullptr
+                         : ws_o + static_cast<size_t>(batch) * shape->num_q_heads * parts *
+                                      shape->head_dim_v;
+  const Kind kind = classify(shape);
+  if (kind == Kind::MlaBf16 || kind == Kind::MlaFp8)
+    return radix_mla_decode_impl(shape, kv, q, req_to_token, rtt_stride, req_rows, seq_lens,
+                                 batch, max_seq_len, use_plan ? plan : nullptr, splits, out,
+                                 lse_out, ws_o, ws_lse, parts, s);
+
+  AttnArgs a = attn_args(shape, kv, q, req_to_token, rtt_stride, req_rows, out, lse_out);
+  a.seq_lens = seq_lens;
+  a.num_splits = splits;
+  a.parts = parts;
+  a.part_base = max_shared;
+  a.ws_o = ws_o;
+  a.ws_lse = ws_lse;
+  const bool bf16 = kind == Kind::GqaBf16;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (use_plan) {
+    a.seg_row = plan->seg_row;
+    a.seg_start = plan->seg_start;
+    a.seg_end = plan->seg_end;
+    a.seg_member_off = plan->seg_member_off;
+    a.seg_members = plan->seg_members;
+    a.seg_member_slot = plan->seg_member_slot;
+    a.num_segments = plan->num_segments;
+    a.req_num_shared = plan->req_num_shared;
+    a.private_start = plan->req_private_start;
+    if (bf16)
+      st = hip_status(radix_launch::mfma(G, true, a, plan->max_members * G, plan->num_segments, s),
+                      "segment launch");
+    else
+      st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, 1, s),
+                      "segment launch");
+    if (st != RADIX_OK) return st;
+  }
+  st = hip_status(radix_launch::valu(bf16, G, 0, a, batch, splits, s), "decode launch");
+  if (st != RADIX_OK || direct) return st;
+  return hip_status(radix_launch::combine(bf16, a, batch, shape->head_dim_v, s), "combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Each case runs a workload's request script through the native tree and the
+gfx950 kernels (extend, shared-segment decode, split-KV decode, combine) and
+compares the outputs with the oracle's exact attention over each request's
+own keys (fp64): max-abs <= 1e-4 for fp32, <= 2e-2 for bf16 I/O with fp32
+accumulation. LSE within 1e-5 / 1e-3.
+"""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from oracle.attention import reference_outputs
+from workloads import agent_branch, chat_decode, chat_tree, config, few_shot, gqa128_shape, tiny_shape
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-4, 1e-5), "bf16": (2e-2, 1e-3)}
+
+
+def _to_np(t):
+    import torch
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+class Checker:
+    """Collects device outputs through the runner's callbacks and checks a sample."""
+
+    def __init__(self, w, extend_sample=None, decode_steps=None, decode_sample=None, seed=0):
+        self.w = w
+        self.rng = np.random.default_rng(seed)
+        self.extend_sample = extend_sample
+        self.decode_steps = decode_steps
+        self.decode_sample = decode_sample
+        self.tol_o, self.tol_l = TOL[w.shape.q_dtype]
+        self.worst = 0.0
+        self.checked = 0
+
+    def _pick(self, n, k):
+        if k is None or k >= n:
+            return np.arange(n)
+        return np.sort(self.rng.choice(n, size=k, replace=False))
+
+    def _cmp(self, o, l, ref_o, ref_l, what):
+        err = np.abs(o - ref_o).max()
+        lerr = np.abs(l - ref_l).max()
+        self.worst = max(self.worst, err)
+        self.checked += 1
+        assert err <= self.tol_o, f"{what}: output max-abs {err}"
+        assert lerr <= self.tol_l, f"{what}: lse max-abs {lerr}"
+
+    def on_extend(self, rnd, out, lse, cu):
+        if out is None:
+            return
+        o_all, l_all = _to_np(out), _to_np(lse)
+        for b in self._pick(len(rnd.admissions), self.extend_sample):
+            a = rnd.admissions[b]
+            if a.prompt_len == a.prefix_len:
+                continue
+            pos = np.arange(a.prefix_len, a.prompt_len)
+            if len(pos) > 64:   # first, last and a random middle sample of positions
+                pos = np.unique(np.concatenate([pos[:8], pos[-8:], self.rng.choice(pos, 24)]))
+            ro, rl = reference_outputs(self.w, a.rid, pos)
+            idx = cu[b] + (pos - a.prefix_len)
+            self._cmp(o_all[idx], l_all[idx], ro, rl, f"extend rid {a.rid}")
+
+    def on_decode(self, rnd, step, out, lse):
+        if self.decode_steps is not None and step not in self.decode_steps:
+            return
+        o_all, l_all = _to_np(out), _to_np(lse)
+        for b in self._pick(len(rnd.admissions), self.decode_sample):
+            a = rnd.admissions[b]
+            pos = np.array([a.prompt_len + step])
+            ro, rl = reference_outputs(self.w, a.rid, pos)
+            self._cmp(o_all[b:b + 1], l_all[b:b + 1], ro, rl, f"decode rid {a.rid} step {step}")
+
+
+def _run(w, checker, **kw):
+    import torch
+    from prefix_shared_kv_radix_amd.runner import Engine
+    print(f"[gpu case] {w.name} {kw}", flush=True)
+    eng = Engine(w, device="cuda", on_extend=checker.on_extend, on_decode=checker.on_decode, **kw)
+    log = eng.run()
+    torch.cuda.synchronize()
+    assert checker.checked > 0
+    print(f"[gpu case] {w.name} ok: {checker.checked} checks, worst {checker.worst:.3g}", flush=True)
+    return log
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("use_plan,splits", [(True, 0), (False, 1), (False, 3), (True, 2)])
+def test_tiny_fp32_all_outputs(use_plan, splits):
+    """Config 1 in full: every extend and decode output of every request."""
+    w = config(1)
+    _run(w, Checker(w), use_plan=use_plan, num_splits=splits)
+
+
+@pytest.mark.parametrize("use_plan,splits", [(True, 0), (False, 1), (False, 5), (True, 3)])
+def test_few_shot_bf16_small(use_plan, splits):
+    """GQA-128 bf16, 300-token shared prefix, 24 requests x 37 new tokens (ragged MFMA
+    tiles), 9 decode steps, all outputs."""
+    w = few_shot(2, gqa128_shape(), 300, 24, 37, 9, q_rows=4096)
+    _run(w, Checker(w), use_plan=use_plan, num_splits=splits)
+
+
+def test_agent_two_level_segments_bf16():
+    """Roots, branches and forks: decode reads two nested shared segments per request."""
+    w = agent_branch(4, gqa128_shape(), 3, 200, 4, 70, 3, 6, q_rows=4096)
+    _run(w, Checker(w, extend_sample=6))
+
+
+def test_chat_tree_under_churn_bf16():
+    """Multi-turn chat with a pool at 40% of the working set: evicted history is
+    recomputed, slot lists are scattered."""
+    w = chat_tree(13, gqa128_shape(), 10, 5, 20, 90, 0.4, q_rows=4096)
+    _run(w, Checker(w, extend_sample=5))
+
+
+def test_chat_decode_scattered_bf16():
+    w = chat_decode(3, gqa128_shape(), 16, 300, 1500, 30, 120, 4, batch_limit=12, q_rows=4096)
+    _run(w, Checker(w))
+
+
+def test_tiny_shapes_gqa_groups_fp32():
+    """Query-head groups 1, 2, 4, 8 on the fp32 path."""
+    import dataclasses
+    for hq, hkv in ((4, 4), (4, 2), (8, 2), (8, 1)):
+        shape = dataclasses.replace(tiny_shape(), num_q_heads=hq, num_kv_heads=hkv)
+        w = few_shot(7, shape, 45, 5, 13, 3, q_rows=256)
+        _run(w, Checker(w))
+
+
+def test_gqa_groups_bf16():
+    import dataclasses
+    for hq, hkv in ((8, 8), (16, 8), (64, 8)):
+        shape = dataclasses.replace(gqa128_shape(), num_q_heads=hq)
+        w = few_shot(8, shape, 130, 6, 21, 3, q_rows=512)
+        _run(w, Checker(w))
+
+
+def test_few_shot_full_size_sampled():
+    """Config 2 at full size (2048-token prefix x 256 requests x 128 tokens, 128 decode
+    steps at batch 256): sampled requests at sampled steps."""
+    w = config(2)
+    _run(w, Checker(w, extend_sample=6, decode_steps={0, 1, 64, 127}, decode_sample=8))
+
+
+def test_agent_full_size_sampled():
+    """Config 4: 16 roots x 4096 (prefill), 128 branches x 512, 512 forks decoding
+    256 steps through two nested shared segments."""
+    w = config(4)
+    _run(w, Checker(w, extend_sample=3, decode_steps={0, 255}, decode_sample=6))
+
+
+def test_chat_tree_full_size_sampled():
+    w = config(3, "A")
+    _run(w, Checker(w, extend_sample=3))
+
+
+def test_chat_decode_full_size_sampled():
+    """Config 3B: 256 decode requests with 1k-8k contexts scattered by churn."""
+    w = config(3, "B")
+    _run(w, Checker(w, decode_steps={0, 31}, decode_sample=8))

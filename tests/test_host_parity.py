@@ -1,0 +1,212 @@
+"""The native host library (C++ pool, radix tree, scheduler) against the oracle.
+
+Slot lists, matched lengths, admission order, decode slots, duplicate counts,
+the final free list and eviction totals must be bit-identical: both follow the
+same reading of the pages (page "49 · RadixAttention, eviction và cache
+churn", §2, §4, §5), but share no code. Runs on the CPU (no GPU calls).
+"""
+import random
+import re
+import os
+
+import numpy as np
+import pytest
+
+from oracle.episode import run_episode
+from prefix_shared_kv_radix_amd import _lib
+from prefix_shared_kv_radix_amd.runner import Engine
+from workloads import (Phase, Workload, _req, agent_branch, chat_decode, chat_tree, config,
+                       cyclic_stream, few_shot, gqa128_shape, mla_groups, tiny_shape)
+
+
+def _compare(w):
+    ref = run_episode(w)
+    got = Engine(w).run()
+    assert len(ref.rounds) == len(got.rounds)
+    for r, g in zip(ref.rounds, got.rounds):
+        assert r.phase == g.phase
+        assert [a.rid for a in r.admissions] == [a.rid for a in g.admissions]
+        for a, b in zip(r.admissions, g.admissions):
+            assert a.prefix_len == b.prefix_len and a.prompt_len == b.prompt_len, a.rid
+            np.testing.assert_array_equal(a.row, b.row)
+        np.testing.assert_array_equal(r.decode_slots, g.decode_slots)
+        np.testing.assert_array_equal(r.already_cached, g.already_cached)
+    np.testing.assert_array_equal(ref.free_list, got.free_list)
+    assert ref.cached_tokens == got.stats.cached_tokens
+    assert ref.evicted_tokens_total == got.stats.evicted_tokens_total
+    assert ref.hits() == got.hits()
+    return ref, got
+
+
+WORKLOADS = {
+    "tiny": lambda: config(1),
+    "few_shot_small": lambda: few_shot(2, gqa128_shape(), 300, 24, 37, 9),
+    "few_shot_full": lambda: config(2),
+    "chat_tree_full": lambda: config(3, "A"),
+    "chat_tree_tight": lambda: chat_tree(13, tiny_shape(), 12, 6, 5, 40, 0.4),
+    "chat_decode_small": lambda: chat_decode(3, tiny_shape(), 12, 100, 600, 16, 64, 5, batch_limit=7),
+    "agent_small": lambda: agent_branch(4, tiny_shape(), 3, 100, 4, 30, 3, 7),
+    "agent_full": lambda: config(4),
+    "cyclic": lambda: config(4, "cyclic"),
+    "grouped": lambda: config(4, "grouped"),
+    "cyclic_lpf": lambda: config(4, "cyclic_lpf"),
+    "mla_small": lambda: mla_groups(5, "bf16", 3, 50, 6, 40, 4, q_rows=64),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_episode_bit_exact(name):
+    _compare(WORKLOADS[name]())
+
+
+def test_churn_numbers_through_native_tree():
+    """0/10 cyclic, 5/10 grouped, 5/10 longest-prefix-first (page 4 §6)."""
+    assert Engine(config(4, "cyclic")).run().hits()[0] == 0
+    assert Engine(config(4, "grouped")).run().hits()[0] == 5
+    assert Engine(config(4, "cyclic_lpf")).run().hits()[0] == 5
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_traces_with_tiny_pools(seed):
+    """Random prompts over a 3-token alphabet, tiny pools, mixed policies and batch
+    limits, with decode steps: heavy splitting and eviction."""
+    rng = random.Random(seed)
+    n = rng.randint(4, 30)
+    reqs = []
+    for i in range(n):
+        L = rng.randint(1, 9)
+        toks = np.array([rng.randint(0, 2) for _ in range(L)], np.int32)
+        outs = np.array([rng.randint(0, 2) for _ in range(3)], np.int32)
+        reqs.append(_req(i, toks, np.arange(L) + 100 * i, outs, np.arange(3) + 100 * i + 50))
+    phases, i = [], 0
+    while i < n:
+        k = rng.randint(1, 6)
+        phases.append(Phase(list(range(i, min(n, i + k))), rng.choice(["fcfs", "lpf"]),
+                            rng.randint(1, 4), rng.randint(0, 3), "host"))
+        i += k
+    pool = rng.randint(16, 40)
+    w = Workload("fuzz", seed, tiny_shape(), pool, reqs, phases, 1, 1, 1)
+    try:
+        ref = run_episode(w)
+    except RuntimeError:
+        with pytest.raises(RuntimeError):
+            Engine(w).run()
+        return
+    _compare(w)
+
+
+# ------------------------------------------------------------ ABI behaviour
+def test_pool_fifo_errors_and_atomicity():
+    p = _lib.KVPool(6)
+    np.testing.assert_array_equal(p.alloc(3), [0, 1, 2])
+    p.free([1, 0])
+    np.testing.assert_array_equal(p.free_list(), [3, 4, 5, 1, 0])
+    for bad in ([3], [6], [-1], [2, 2]):
+        with pytest.raises(_lib.RadixError) as e:
+            p.free(bad)
+        assert e.value.status == _lib.E_INVAL
+    np.testing.assert_array_equal(p.free_list(), [3, 4, 5, 1, 0])   # unchanged
+    with pytest.raises(_lib.NoMemory):
+        p.alloc(6)
+    assert p.num_free() == 5
+
+
+def test_tree_nomem_leaves_state_unchanged():
+    p = _lib.KVPool(10)
+    t = _lib.RadixTree(p)
+    m, row, node = t.admit(np.arange(6))
+    before = (p.free_list().tolist(), t.stats().tick)
+    with pytest.raises(_lib.NoMemory):
+        t.alloc(5)
+    assert (p.free_list().tolist(), t.stats().tick) == before
+    with pytest.raises(_lib.NoMemory):
+        t.admit(np.arange(100, 111))       # 11 tokens > 10 slots
+    t.finish(np.arange(6), row, m, node)
+    assert len(t.alloc(10)) == 10          # everything evictable now
+
+
+def test_unlock_below_zero_and_bad_handles():
+    p = _lib.KVPool(10)
+    t = _lib.RadixTree(p)
+    m, row, node = t.admit(np.arange(3))
+    t.finish(np.arange(3), row, m, node)
+    m, row, node = t.admit(np.arange(5))        # matches 3 tokens: pins a real node
+    assert m == 3 and node != 0
+    t.finish(np.arange(5), row, m, node)
+    with pytest.raises(_lib.RadixError):
+        t.unlock(node)
+    with pytest.raises(_lib.RadixError):
+        t.lock(12345)
+
+
+def test_decode_plan_matches_tree_structure():
+    """Shared segments follow the radix nodes shared by running requests."""
+    w = agent_branch(4, tiny_shape(), 3, 40, 4, 10, 3, 2)
+    eng = Engine(w, use_plan=True)
+    log = eng.run()
+    rnd = log.rounds[-1]
+    plan = rnd.plan
+    # three roots x 4 branches x 3 forks: root segments (12 members) then branch segments (3)
+    assert plan.num_segments == 3 + 12
+    sizes = sorted(np.diff(plan.seg_member_off).tolist())
+    assert sizes == [3] * 12 + [12] * 3
+    assert set(plan.req_num_shared.tolist()) == {2}
+    assert set(plan.req_private_start.tolist()) == {50}
+    for s in range(plan.num_segments):
+        mem = plan.seg_members[plan.seg_member_off[s]:plan.seg_member_off[s + 1]]
+        rows = [rnd.admissions[b].row[plan.seg_start[s]:plan.seg_end[s]] for b in mem]
+        for r in rows[1:]:
+            np.testing.assert_array_equal(r, rows[0])   # members share the slots
+        np.testing.assert_array_equal(rnd.admissions[plan.seg_row[s]].row[plan.seg_start[s]:plan.seg_end[s]],
+                                      rows[0])
+
+
+def test_decode_plan_brute_force():
+    """Random batches: for each pair of requests, the shared segments they have in
+    common cover exactly the prefix of identical slots up to the shallower private start."""
+    for seed in range(20):
+        rng = random.Random(seed)
+        p = _lib.KVPool(4000)
+        t = _lib.RadixTree(p)
+        base = [[rng.randint(0, 2) for _ in range(rng.randint(1, 6))] for _ in range(4)]
+        for s in base:
+            m, row, node = t.admit(s)
+            t.finish(s, row, m, node)
+        prompts = []
+        for _ in range(rng.randint(2, 10)):
+            b = rng.choice(base)
+            prompts.append(b[:rng.randint(0, len(b))] + [rng.randint(0, 2) for _ in range(rng.randint(0, 3))])
+        adm = [t.admit(pr) for pr in prompts]
+        plan = t.decode_plan([a[2] for a in adm])
+        for i in range(len(adm)):
+            segs = [s for s in range(plan.num_segments)
+                    if i in plan.seg_members[plan.seg_member_off[s]:plan.seg_member_off[s + 1]]]
+            cover = sorted((plan.seg_start[s], plan.seg_end[s]) for s in segs)
+            pos = 0
+            for a0, a1 in cover:
+                assert a0 == pos
+                pos = a1
+            assert pos == plan.req_private_start[i] <= adm[i][0]
+            for s in segs:
+                mem = plan.seg_members[plan.seg_member_off[s]:plan.seg_member_off[s + 1]]
+                assert len(mem) >= 2
+                for j in mem:
+                    np.testing.assert_array_equal(adm[j][1][plan.seg_start[s]:plan.seg_end[s]],
+                                                  adm[i][1][plan.seg_start[s]:plan.seg_end[s]])
+
+
+def test_library_exports_every_declared_symbol():
+    """Every function declared in include/*.h is exported by the built library."""
+    import ctypes
+    hdr_dir = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+    names = set()
+    for f in os.listdir(hdr_dir):
+        if f.endswith(".h"):
+            text = open(os.path.join(hdr_dir, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(radix_[a-z0-9_]+)\s*\(", text))
+    assert len(names) > 20
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(_lib.exported_symbols()) <= names
