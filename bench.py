@@ -1,0 +1,359 @@
+"""Throughput of prefix-shared KV attention over a radix-tree slot pool on one MI355X.
+
+One step = one whole episode of the workload: for every round, order and admit
+the requests through the native radix tree (match, pin, allocate with LRU
+eviction), extend them (store new K/V + attention against the cached prefix),
+run every decode step (one new slot per request from the tree, store, decode
+attention over shared segments + private tails), and finish them (insert,
+free duplicates, unpin). Query/K/V inputs are staged in HBM before the timed
+region; slot lists are produced inside it by the host tree and copied over.
+
+Prints one JSON line. `value` = decode tokens generated per second of episode
+time (whole job); the breakdown, per-kernel event timings, the roofline of the
+dominant kernel and the CPU oracle's rate on a bounded sample are included.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--config", default="2", help="2 (default), 1, 3A, 3B, 4, 5bf16, 5fp8")
+    p.add_argument("--no-plan", action="store_true", help="decode without shared segments")
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def workload_of(name):
+    from workloads import config
+    table = {"1": (1, ""), "2": (2, ""), "3A": (3, "A"), "3B": (3, "B"), "4": (4, ""),
+             "5bf16": (5, "bf16"), "5fp8": (5, "fp8")}
+    n, v = table[name]
+    return config(n, v)
+
+
+class Episode:
+    """Pre-staged device inputs for every round of a workload, and one timed pass."""
+
+    def __init__(self, w, use_plan, splits):
+        import torch
+        from prefix_shared_kv_radix_amd import _lib
+        from prefix_shared_kv_radix_amd.runner import DeviceState, Engine
+        self.torch, self._lib = torch, _lib
+        self.w, self.use_plan, self.splits = w, use_plan, splits
+        dry = Engine(w).run()              # host-only pass: the rounds are deterministic
+        self.rounds = dry.rounds
+        dev = "cuda"
+        max_batch = max(len(r.admissions) for r in dry.rounds)
+        self.stride = max(len(r.tokens) + len(r.out_tokens) for r in w.requests)
+        self.d = DeviceState(w, dev, max_batch, self.stride)
+        d, s = self.d, w.shape
+        self.staged = []
+        self.max_ws = 0
+        for r_idx, rnd in enumerate(dry.rounds):
+            ph = w.phases[rnd.phase]
+            adm = rnd.admissions
+            B = len(adm)
+            st = {"B": B, "ph": ph, "rids": [a.rid for a in adm],
+                  "prompts": [w.requests[a.rid].tokens for a in adm],
+                  "seqs": [np.concatenate([w.requests[a.rid].tokens,
+                                           w.requests[a.rid].out_tokens[:ph.n_decode]]) for a in adm],
+                  "prompt_len": np.array([a.prompt_len for a in adm], np.int32),
+                  "prefix_len": np.array([a.prefix_len for a in adm], np.int64)}
+            el = st["prompt_len"] - st["prefix_len"].astype(np.int32)
+            cu = np.zeros(B + 1, np.int32)
+            cu[1:] = np.cumsum(el)
+            st.update(el=el, cu=cu, T=int(cu[-1]), max_e=int(el.max()) if B else 0,
+                      pl_dev=d.i32(st["prefix_len"]), el_dev=d.i32(el), cu_dev=d.i32(cu))
+            if ph.extend != "host" and st["T"]:
+                ids = np.concatenate([w.requests[a.rid].kv_ids[a.prefix_len:] for a in adm])
+                rows = d.rows_of(w, ids)
+                st["k_new"] = d.k_tab[rows]
+                st["v_new"] = None if d.v_tab is None else d.v_tab[rows]
+                st["sc_new"] = None if d.sc_tab is None else d.sc_tab[rows]
+                st["slots_hint"] = None
+                if ph.extend == "attend":
+                    qi = np.concatenate([w.q_index(a.rid, np.arange(a.prefix_len, a.prompt_len))
+                                         for a in adm])
+                    st["q"] = d.q_tab[torch.from_numpy(qi).to(dev)]
+                    st["out"] = torch.empty((st["T"], s.num_q_heads, s.head_dim_v),
+                                            dtype=d.q_dtype, device=dev)
+            if ph.n_decode:
+                n = ph.n_decode
+                qi = np.stack([w.q_index(a.rid, a.prompt_len + np.arange(n)) for a in adm], 1)
+                st["dq"] = d.q_tab[torch.from_numpy(qi.reshape(-1)).to(dev)].view(
+                    n, B, s.num_q_heads, s.head_dim_qk)
+                ids = np.stack([w.requests[a.rid].out_kv_ids[:n] for a in adm], 1)
+                rows = d.rows_of(w, ids.reshape(-1))
+                st["dk"] = d.k_tab[rows].view(n, B, *d.k_tab.shape[1:])
+                st["dv"] = None if d.v_tab is None else d.v_tab[rows].view(n, B, *d.v_tab.shape[1:])
+                st["dsc"] = None if d.sc_tab is None else d.sc_tab[rows].view(n, B)
+                seq = st["prompt_len"][None, :] + 1 + np.arange(n)[:, None]
+                st["seq_dev"] = d.i32(seq)
+                st["seq_host"] = seq
+                st["dout"] = torch.empty((B, s.num_q_heads, s.head_dim_v), dtype=d.q_dtype, device=dev)
+                st["slot_pin"] = torch.empty((2, n, B), dtype=torch.int32, pin_memory=True)
+                st["slot_dev"] = torch.empty((n, B), dtype=torch.int32, device=dev)
+                max_shared = 0
+                if use_plan and rnd.plan is not None:
+                    max_shared = rnd.plan.max_shared
+                self.max_ws = max(self.max_ws, _lib.decode_workspace_size(
+                    d.shape, B, int(seq.max()), max_shared, splits))
+            self.staged.append(st)
+        self.ws = torch.empty(max(self.max_ws // 4, 1), dtype=torch.float32, device=dev)
+        self.rtt_pin = torch.empty((2, max_batch, self.stride), dtype=torch.int32, pin_memory=True)
+        self.parity = 0
+        self.done_evt = [None, None]
+        self.marks = []
+
+    def run(self, mark=False):
+        """One episode; returns nothing (all work is enqueued on the current stream)."""
+        torch, _lib, d, w = self.torch, self._lib, self.d, self.w
+        par = self.parity
+        self.parity ^= 1
+        if self.done_evt[par] is not None:
+            self.done_evt[par].synchronize()       # pinned staging of two episodes ago is free
+        pool = _lib.KVPool(w.pool_slots)
+        tree = _lib.RadixTree(pool)
+        rtt_pin = self.rtt_pin[par]
+        marks = []
+        for st in self.staged:
+            ph, B = st["ph"], st["B"]
+            k, rows, pl, nodes = tree.admit_batch(st["prompts"], B, self.stride)
+            if k != B or not np.array_equal(pl, st["prefix_len"]):
+                raise RuntimeError("episode diverged from its dry run")
+            plan_dev, keep = (None, [])
+            if ph.n_decode and self.use_plan and B > 1:
+                plan_dev, keep = _lib.device_plan(tree.decode_plan(nodes), d.device)
+            if ph.extend != "host":
+                rtt_pin[:B].copy_(torch.from_numpy(rows))
+                d.rtt[:B].copy_(rtt_pin[:B], non_blocking=True)
+            if mark:
+                marks.append(("extend_start", torch.cuda.Event(enable_timing=True)))
+                marks[-1][1].record()
+            if ph.extend != "host" and st["T"]:
+                if ph.extend == "attend":
+                    _lib.attn_extend(d.shape, d.kv, st["q"], st["k_new"], st["v_new"], st["sc_new"],
+                                     d.rtt, None, st["pl_dev"], st["el_dev"], st["cu_dev"], B,
+                                     st["T"], st["max_e"], st["out"], None)
+                else:
+                    slots = np.concatenate([rows[b, st["prefix_len"][b]:st["prompt_len"][b]]
+                                            for b in range(B)])
+                    _lib.kv_store(d.shape, d.kv, st["k_new"], st["v_new"], st["sc_new"], d.i32(slots))
+            if mark:
+                marks.append(("decode_start", torch.cuda.Event(enable_timing=True)))
+                marks[-1][1].record()
+            n = ph.n_decode
+            if n:
+                pin = st["slot_pin"][par]
+                for s in range(n):
+                    slots = tree.alloc(B)
+                    rows[np.arange(B), st["prompt_len"] + s] = slots
+                    pin[s].copy_(torch.from_numpy(slots))
+                    st["slot_dev"][s].copy_(pin[s], non_blocking=True)
+                    _lib.attn_decode(d.shape, d.kv, st["dq"][s], st["dk"][s],
+                                     None if st["dv"] is None else st["dv"][s],
+                                     None if st["dsc"] is None else st["dsc"][s], st["slot_dev"][s],
+                                     d.rtt, None, st["seq_dev"][s], B, int(st["seq_host"][s].max()),
+                                     plan_dev, self.splits, st["dout"], None, self.ws)
+            if mark:
+                marks.append(("round_end", torch.cuda.Event(enable_timing=True)))
+                marks[-1][1].record()
+            tree.finish_batch(st["seqs"], rows, pl, nodes)
+            del keep
+        evt = torch.cuda.Event()
+        evt.record()
+        self.done_evt[par] = evt
+        if mark:
+            self.marks.append(marks)
+        tree.close()
+        pool.close()
+
+
+def algorithmic(w, ep, name):
+    """Algorithmic work of one episode for a kernel family: (bytes, flops)."""
+    s = w.shape
+    eb_kv = {"f32": 4, "bf16": 2, "fp8": 1}[s.kv_dtype]
+    eb_q = {"f32": 4, "bf16": 2}[s.q_dtype]
+    row_kv = s.num_kv_heads * (s.head_dim_qk + (0 if s.v_is_k_prefix else s.head_dim_v)) * eb_kv \
+        + (4 if s.kv_dtype == "fp8" else 0)
+    q_row = s.num_q_heads * s.head_dim_qk * eb_q
+    o_row = s.num_q_heads * s.head_dim_v * eb_q
+    byt, flop = 0.0, 0.0
+    for st, rnd in zip(ep.staged, ep.rounds):
+        ph, B = st["ph"], st["B"]
+        if name == "extend_mfma" and ph.extend == "attend":
+            for a in rnd.admissions:
+                P, E = a.prefix_len, a.prompt_len - a.prefix_len
+                pairs = E * P + E * (E + 1) / 2
+                flop += 2.0 * s.num_q_heads * (s.head_dim_qk + s.head_dim_v) * pairs
+                byt += (P + E) * row_kv + E * (q_row + o_row)
+        if not ph.n_decode:
+            continue
+        plan = rnd.plan if ep.use_plan and B > 1 else None
+        ps = plan.req_private_start if plan is not None else np.zeros(B, np.int32)
+        for step in range(ph.n_decode):
+            L = st["prompt_len"] + step + 1
+            if name in ("decode_tail_valu", "mla_decode"):
+                keys = (L - ps).sum()
+                byt += keys * (row_kv + 4) + B * q_row
+                flop += 2.0 * s.num_q_heads * (s.head_dim_qk + s.head_dim_v) * float(L.sum())
+            if name == "segment_mfma" and plan is not None:
+                seg_keys = (plan.seg_end - plan.seg_start).sum()
+                entries = len(plan.seg_members)
+                byt += seg_keys * (row_kv + 4) + entries * q_row
+            if name == "kv_store":
+                byt += 2 * B * row_kv
+    return byt, flop
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, on a bounded sample: decode attention of the
+    workload's decode requests at their first step, request after request."""
+    from threadpoolctl import threadpool_info
+    from oracle.attention import reference_outputs
+    from oracle.episode import run_episode
+    t0 = time.perf_counter()
+    log = run_episode(w)
+    t_host = time.perf_counter() - t0
+    dec = [(a, len(rnd.decode_slots)) for rnd in log.rounds for a in rnd.admissions
+           if len(rnd.decode_slots)]
+    n = 0
+    t0 = time.perf_counter()
+    steps = max(s for _, s in dec)
+    for step in range(steps):
+        for a, ns in dec:
+            if step < ns:
+                reference_outputs(w, a.rid, np.array([a.prompt_len + step]))
+                n += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n / dt, "unit": "decode tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} decode queries (from step 0 on, L~{int(dec[0][0].prompt_len) + 1}) of "
+                      f"{w.name} in {dt:.1f}s, fp64 exact attention; oracle tree+pool episode "
+                      f"{t_host:.2f}s",
+            "host_cores_visible": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requests shard across GPUs with no exchange inside attention); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from prefix_shared_kv_radix_amd import _lib
+    _lib.load()
+    torch.cuda.set_device(0)
+    w = workload_of(args.config)
+    ep = Episode(w, not args.no_plan, args.splits)
+    torch.cuda.synchronize()
+    print(f"[bench] staged {w.name}: {len(ep.rounds)} rounds", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        ep.run()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    _lib.profile_enable(1 << 17)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ep.run(mark=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = _lib.profile_read(1 << 17)
+    _lib.profile_enable(0)
+    print(f"[bench] timed {args.steps} steps in {t1 - t0:.3f}s", file=sys.stderr, flush=True)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_tokens = sum(st["B"] * st["ph"].n_decode for st in ep.staged)
+    ext_tokens = sum(st["T"] for st in ep.staged if st["ph"].extend == "attend")
+    ext_ms = dec_ms = 0.0
+    for seq in ep.marks:
+        for i in range(0, len(seq), 3):
+            ext_ms += seq[i][1].elapsed_time(seq[i + 1][1])
+            dec_ms += seq[i + 1][1].elapsed_time(seq[i + 2][1])
+    ext_ms /= args.steps
+    dec_ms /= args.steps
+    kern = {}
+    for name, t in prof:
+        k = kern.setdefault(name, [0, 0.0])
+        k[0] += 1
+        k[1] += t
+    kernels = {n: {"launches": c // args.steps, "ms_per_step": t / args.steps, "avg_us": 1e3 * t / c}
+               for n, (c, t) in kern.items()}
+    dom = max(kern, key=lambda n: kern[n][1])
+    byt, flop = algorithmic(w, ep, dom)
+    t_dom = kern[dom][1] / args.steps / 1e3          # seconds per episode in that kernel
+    if dom in ("extend_mfma",):
+        roof = {"bound": "mfma", "achieved": flop / t_dom / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byt / t_dom / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = 1e3 * kern[dom][1] / kern[dom][0]
+    roof["traffic"] = None
+    # decode-phase aggregate HBM rate over all decode kernels' algorithmic bytes
+    dec_bytes = sum(algorithmic(w, ep, n)[0] for n in ("decode_tail_valu", "segment_mfma",
+                                                         "kv_store", "mla_decode") if n in kern)
+    ext_flops = algorithmic(w, ep, "extend_mfma")[1]
+    out = {
+        "metric": "decode tokens/s + achieved HBM GB/s (% peak), prefix-shared KV attention",
+        "value": dec_tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.shape.kv_dtype if w.shape.kv_dtype != "fp8" else "fp8-kv/bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pool_slots": w.pool_slots,
+                   "q_heads": w.shape.num_q_heads, "kv_heads": w.shape.num_kv_heads,
+                   "head_dim": w.shape.head_dim_qk, "decode_tokens_per_step": dec_tokens,
+                   "extend_tokens_per_step": ext_tokens, "shared_segments": not args.no_plan},
+        "extend_ms_per_step": ext_ms,
+        "decode_ms_per_step": dec_ms,
+        "decode_only_tokens_per_s": dec_tokens / (dec_ms / 1e3) if dec_ms else None,
+        "extend_tokens_per_s": ext_tokens / (ext_ms / 1e3) if ext_ms else None,
+        "extend_tflops": ext_flops / (ext_ms / 1e3) / 1e12 if ext_ms else None,
+        "decode_algorithmic_gbps": dec_bytes / (dec_ms / 1e3) / 1e9 if dec_ms else None,
+        "decode_hbm_frac_of_peak": dec_bytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBPS if dec_ms else None,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

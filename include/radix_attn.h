@@ -154,6 +154,26 @@ radix_status radix_req_admit(radix_tree *tree, const int32_t *tok, int64_t n, in
 radix_status radix_req_finish(radix_tree *tree, const int32_t *tok, const int32_t *row, int64_t n,
                               int64_t prefix_len, radix_node node, int64_t *already_cached);
 
+/* Batched lifecycle for a round (same semantics as calling radix_req_admit /
+ * radix_req_finish per request in order). Request i's tokens are
+ * tok[tok_off[i] .. tok_off[i+1]).
+ * admit_batch: admits requests 0, 1, ... in order until max_batch are admitted or
+ *   one cannot get its slots (it is left waiting, un-pinned); *admitted receives the
+ *   count. Admitted request i's slots go to rows[i*row_stride ...], its matched
+ *   length to prefix_len[i], its pinned node to nodes[i]. row_stride must be at
+ *   least the longest prompt.
+ * finish_batch: finishes n requests; request i's tokens (prompt + outputs) are
+ *   tok[tok_off[i] .. tok_off[i+1]) and its slots rows[i*row_stride ...] of the same
+ *   count; already_cached[i] (may be NULL) receives the insert's count. */
+radix_status radix_req_admit_batch(radix_tree *tree, const int32_t *tok, const int64_t *tok_off,
+                                   int64_t n, int64_t max_batch, int32_t *rows,
+                                   int64_t row_stride, int64_t *prefix_len, radix_node *nodes,
+                                   int64_t *admitted);
+radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const int64_t *tok_off,
+                                    const int32_t *rows, int64_t row_stride,
+                                    const int64_t *prefix_len, const radix_node *nodes, int64_t n,
+                                    int64_t *already_cached);
+
 /* ======================================================================
  * Decode plan from the tree: shared segments.
  * Requests running on one tree node read the same slots for that node's
@@ -284,6 +304,19 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
                                int32_t max_seq_len, const radix_decode_plan *plan,
                                int32_t num_splits, void *out, float *lse_out, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* ======================================================================
+ * Kernel timing for measurement tools. While enabled, every kernel the
+ * attention calls launch is bracketed by two HIP events recorded on the
+ * launch stream (up to `capacity` launches; later ones are not recorded).
+ * radix_profile_enable(0) disables timing and releases the events.
+ * radix_profile_read waits for the recorded events, writes up to `cap`
+ * (kernel id, milliseconds) pairs and starts a new recording.
+ * ====================================================================== */
+radix_status radix_profile_enable(int32_t capacity);
+radix_status radix_profile_read(int32_t *kernel_ids, float *ms, int32_t cap, int32_t *count);
+/* Name of a kernel id reported by radix_profile_read ("" if unknown). */
+const char *radix_kernel_name(int32_t kernel_id);
 
 #ifdef __cplusplus
 }

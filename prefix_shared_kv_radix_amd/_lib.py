@@ -81,6 +81,13 @@ _SIGS = {
     "radix_sched_order": (C.c_int, [_vp, C.POINTER(_i32p), _i64p, C.c_int64, C.c_int32, _i64p]),
     "radix_req_admit": (C.c_int, [_vp, _i32p, C.c_int64, _i32p, _i64p, _i64p]),
     "radix_req_finish": (C.c_int, [_vp, _i32p, _i32p, C.c_int64, C.c_int64, C.c_int64, _i64p]),
+    "radix_req_admit_batch": (C.c_int, [_vp, _i32p, _i64p, C.c_int64, C.c_int64, _i32p, C.c_int64,
+                                        _i64p, _i64p, _i64p]),
+    "radix_req_finish_batch": (C.c_int, [_vp, _i32p, _i64p, _i32p, C.c_int64, _i64p, _i64p,
+                                         C.c_int64, _i64p]),
+    "radix_profile_enable": (C.c_int, [C.c_int32]),
+    "radix_profile_read": (C.c_int, [_i32p, C.POINTER(C.c_float), C.c_int32, _i32p]),
+    "radix_kernel_name": (C.c_char_p, [C.c_int32]),
     "radix_tree_decode_plan": (C.c_int, [_vp, _i64p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                          _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
                                          _i32p, _i32p, _i32p, _i32p]),
@@ -261,6 +268,45 @@ class RadixTree:
                                        C.byref(c)))
         return c.value
 
+    def admit_batch(self, prompts, max_batch: int, row_stride: int):
+        """Admit prompts in order until max_batch or a request cannot get its slots.
+        Returns (count, rows [count, row_stride], prefix_len [count], nodes [count])."""
+        n = min(len(prompts), int(max_batch))
+        prompts = prompts[:n]
+        off = np.zeros(n + 1, np.int64)
+        off[1:] = np.cumsum([len(p) for p in prompts])
+        flat = np.ascontiguousarray(np.concatenate(prompts) if n else np.zeros(1, np.int32),
+                                    dtype=np.int32)
+        rows = np.zeros((max(n, 1), int(row_stride)), np.int32)
+        pl = np.zeros(max(n, 1), np.int64)
+        nodes = np.zeros(max(n, 1), np.int64)
+        k = C.c_int64()
+        _check(load().radix_req_admit_batch(self.h, flat.ctypes.data_as(_i32p),
+                                            off.ctypes.data_as(_i64p), n, n,
+                                            rows.ctypes.data_as(_i32p), int(row_stride),
+                                            pl.ctypes.data_as(_i64p), nodes.ctypes.data_as(_i64p),
+                                            C.byref(k)))
+        k = k.value
+        return k, rows[:k], pl[:k], nodes[:k]
+
+    def finish_batch(self, seqs, rows, prefix_len, nodes):
+        """Finish requests: seqs[i] = prompt + outputs, rows[i, :len(seqs[i])] their slots."""
+        n = len(seqs)
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        off = np.zeros(n + 1, np.int64)
+        off[1:] = np.cumsum([len(x) for x in seqs])
+        flat = np.ascontiguousarray(np.concatenate(seqs) if n else np.zeros(1, np.int32),
+                                    dtype=np.int32)
+        pl = np.ascontiguousarray(prefix_len, dtype=np.int64)
+        nd = np.ascontiguousarray(nodes, dtype=np.int64)
+        out = np.zeros(max(n, 1), np.int64)
+        _check(load().radix_req_finish_batch(self.h, flat.ctypes.data_as(_i32p),
+                                             off.ctypes.data_as(_i64p), rows.ctypes.data_as(_i32p),
+                                             rows.shape[1] if rows.ndim == 2 else 0,
+                                             pl.ctypes.data_as(_i64p), nd.ctypes.data_as(_i64p), n,
+                                             out.ctypes.data_as(_i64p)))
+        return out[:n]
+
     def decode_plan(self, nodes, min_members: int = 2):
         """Shared-segment plan (host arrays) for requests admitted at `nodes`."""
         nodes = np.ascontiguousarray(nodes, dtype=np.int64)
@@ -380,3 +426,19 @@ def attn_decode(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token, 
         _ptr(new_slots), _ptr(req_to_token), int(req_to_token.shape[1]), _ptr(req_rows),
         _ptr(seq_lens), int(batch), int(max_seq_len), None if plan is None else C.byref(plan),
         int(num_splits), _ptr(out), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------- timing
+def profile_enable(capacity: int) -> None:
+    _check(load().radix_profile_enable(int(capacity)))
+
+
+def profile_read(cap: int = 1 << 16):
+    """[(kernel name, milliseconds)] for the launches recorded since the last read."""
+    ids = np.zeros(cap, np.int32)
+    ms = np.zeros(cap, np.float32)
+    n = C.c_int32()
+    _check(load().radix_profile_read(ids.ctypes.data_as(_i32p),
+                                     ms.ctypes.data_as(C.POINTER(C.c_float)), cap, C.byref(n)))
+    lib = load()
+    return [(lib.radix_kernel_name(int(i)).decode(), float(t)) for i, t in zip(ids[:n.value], ms[:n.value])]

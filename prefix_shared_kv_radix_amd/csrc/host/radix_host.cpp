@@ -497,6 +497,52 @@ radix_status radix_req_finish(radix_tree *tree, const int32_t *tok, const int32_
   return tree->t.unlock(static_cast<int32_t>(node));
 }
 
+radix_status radix_req_admit_batch(radix_tree *tree, const int32_t *tok, const int64_t *tok_off,
+                                   int64_t n, int64_t max_batch, int32_t *rows,
+                                   int64_t row_stride, int64_t *prefix_len, radix_node *nodes,
+                                   int64_t *admitted) {
+  RADIX_REQUIRE(tree && admitted && n >= 0 && max_batch >= 0 && row_stride >= 0, "bad arguments");
+  RADIX_REQUIRE(n == 0 || (tok_off && tok && rows && prefix_len && nodes), "bad arguments");
+  for (int64_t i = 0; i < n; ++i)
+    RADIX_REQUIRE(tok_off[i + 1] >= tok_off[i] && tok_off[i + 1] - tok_off[i] <= row_stride,
+                  "request longer than row_stride");
+  int64_t k = 0;
+  for (int64_t i = 0; i < n && k < max_batch; ++i) {
+    const int64_t len = tok_off[i + 1] - tok_off[i];
+    int64_t m = 0;
+    radix_node node = 0;
+    radix_status st = radix_req_admit(tree, tok + tok_off[i], len, rows + k * row_stride, &m, &node);
+    if (st == RADIX_E_NOMEM) break;
+    if (st != RADIX_OK) {
+      *admitted = k;
+      return st;
+    }
+    prefix_len[k] = m;
+    nodes[k] = node;
+    ++k;
+  }
+  *admitted = k;
+  return RADIX_OK;
+}
+
+radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const int64_t *tok_off,
+                                    const int32_t *rows, int64_t row_stride,
+                                    const int64_t *prefix_len, const radix_node *nodes, int64_t n,
+                                    int64_t *already_cached) {
+  RADIX_REQUIRE(tree && n >= 0, "bad arguments");
+  RADIX_REQUIRE(n == 0 || (tok && tok_off && rows && prefix_len && nodes), "bad arguments");
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t len = tok_off[i + 1] - tok_off[i];
+    RADIX_REQUIRE(len >= 0 && len <= row_stride, "request longer than row_stride");
+    int64_t c = 0;
+    radix_status st = radix_req_finish(tree, tok + tok_off[i], rows + i * row_stride, len,
+                                       prefix_len[i], nodes[i], &c);
+    if (st != RADIX_OK) return st;
+    if (already_cached) already_cached[i] = c;
+  }
+  return RADIX_OK;
+}
+
 radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *nodes,
                                     int32_t batch, int32_t min_members, int32_t cap_seg,
                                     int32_t cap_mem, int32_t *seg_row, int32_t *seg_start,

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <string>
+#include <vector>
 
 #include "attn_args.hpp"
 #include "host/radix_host.hpp"
@@ -95,6 +96,46 @@ AttnArgs attn_args(const radix_attn_shape *s, const radix_kv_buffers *kv, const 
   return a;
 }
 
+// ---------------------------------------------------------------- event timing
+enum KernelId {
+  K_STORE = 0,
+  K_DECODE_TAIL = 1,
+  K_EXTEND_VALU = 2,
+  K_SEGMENT_VALU = 3,
+  K_EXTEND_MFMA = 4,
+  K_SEGMENT_MFMA = 5,
+  K_COMBINE = 6,
+  K_MLA_DECODE = 7,
+  K_MLA_COMBINE = 8,
+  K_COUNT = 9
+};
+const char *const kKernelNames[K_COUNT] = {
+    "kv_store", "decode_tail_valu", "extend_valu", "segment_valu", "extend_mfma",
+    "segment_mfma", "combine", "mla_decode", "mla_combine"};
+
+struct Profiler {
+  std::vector<hipEvent_t> ev;
+  std::vector<int32_t> ids;
+  int32_t cap = 0, used = 0;
+};
+Profiler g_prof;
+
+// Brackets one launch with events on its stream while timing is enabled.
+struct Timed {
+  int32_t slot = -1;
+  hipStream_t s;
+  Timed(int32_t id, hipStream_t stream) : s(stream) {
+    if (g_prof.used < g_prof.cap) {
+      slot = g_prof.used++;
+      g_prof.ids[slot] = id;
+      hipEventRecord(g_prof.ev[2 * slot], s);
+    }
+  }
+  ~Timed() {
+    if (slot >= 0) hipEventRecord(g_prof.ev[2 * slot + 1], s);
+  }
+};
+
 int auto_splits(int batch, int hkv, int max_seq_len) {
   const int target = 2048;  // resident blocks to fill 256 CUs several times over
   int s = (target + batch * hkv - 1) / (batch * hkv > 0 ? batch * hkv : 1);
@@ -142,6 +183,7 @@ radix_status radix_kv_store(const radix_attn_shape *shape, const radix_kv_buffer
   StoreArgs a = store_args(shape, kv, k_new, v_new, scale_new);
   a.slots = slots;
   a.mode = 0;
+  Timed t(K_STORE, static_cast<hipStream_t>(stream));
   return hip_status(radix_launch::kv_store(a, num_tokens, static_cast<hipStream_t>(stream)),
                     "kv_store launch");
 }
@@ -184,6 +226,7 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
     sa.cu_extend = cu_extend;
     sa.batch = batch;
     sa.mode = 2;
+    Timed t(K_STORE, s);
     st = hip_status(radix_launch::kv_store(sa, total_extend, s), "kv_store launch");
     if (st != RADIX_OK) return st;
   }
@@ -194,8 +237,11 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
   a.batch = batch;
   a.num_splits = 1;
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  if (classify(shape) == Kind::GqaBf16)
+  if (classify(shape) == Kind::GqaBf16) {
+    Timed t(K_EXTEND_MFMA, s);
     return hip_status(radix_launch::mfma(G, false, a, max_extend * G, batch, s), "extend launch");
+  }
+  Timed t(K_EXTEND_VALU, s);
   return hip_status(radix_launch::valu(false, G, 1, a, total_extend, 1, s), "extend launch");
 }
 
@@ -242,6 +288,7 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     sa.req_rows = req_rows;
     sa.seq_lens = seq_lens;
     sa.mode = new_slots ? 1 : 3;
+    Timed t(K_STORE, s);
     st = hip_status(radix_launch::kv_store(sa, batch, s), "kv_store launch");
     if (st != RADIX_OK) return st;
   }
@@ -275,17 +322,63 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     a.num_segments = plan->num_segments;
     a.req_num_shared = plan->req_num_shared;
     a.private_start = plan->req_private_start;
-    if (bf16)
+    if (bf16) {
+      Timed t(K_SEGMENT_MFMA, s);
       st = hip_status(radix_launch::mfma(G, true, a, plan->max_members * G, plan->num_segments, s),
                       "segment launch");
-    else
+    } else {
+      Timed t(K_SEGMENT_VALU, s);
       st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, 1, s),
                       "segment launch");
+    }
     if (st != RADIX_OK) return st;
   }
-  st = hip_status(radix_launch::valu(bf16, G, 0, a, batch, splits, s), "decode launch");
+  {
+    Timed t(K_DECODE_TAIL, s);
+    st = hip_status(radix_launch::valu(bf16, G, 0, a, batch, splits, s), "decode launch");
+  }
   if (st != RADIX_OK || direct) return st;
+  Timed t(K_COMBINE, s);
   return hip_status(radix_launch::combine(bf16, a, batch, shape->head_dim_v, s), "combine launch");
+}
+
+radix_status radix_profile_enable(int32_t capacity) {
+  REQUIRE(capacity >= 0, "negative profiling capacity");
+  for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.ids.assign(capacity, 0);
+  g_prof.cap = 0;
+  g_prof.used = 0;
+  for (int32_t i = 0; i < 2 * capacity; ++i) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      for (hipEvent_t x : g_prof.ev) hipEventDestroy(x);
+      g_prof.ev.clear();
+      return hip_status(err, "hipEventCreate");
+    }
+    g_prof.ev.push_back(e);
+  }
+  g_prof.cap = capacity;
+  return RADIX_OK;
+}
+
+radix_status radix_profile_read(int32_t *kernel_ids, float *ms, int32_t cap, int32_t *count) {
+  REQUIRE(count && cap >= 0 && (cap == 0 || (kernel_ids && ms)), "bad profiling read");
+  const int32_t n = g_prof.used < cap ? g_prof.used : cap;
+  for (int32_t i = 0; i < n; ++i) {
+    hipError_t err = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms[i], g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (err != hipSuccess) return hip_status(err, "event timing");
+    kernel_ids[i] = g_prof.ids[i];
+  }
+  *count = n;
+  g_prof.used = 0;
+  return RADIX_OK;
+}
+
+const char *radix_kernel_name(int32_t kernel_id) {
+  return (kernel_id >= 0 && kernel_id < K_COUNT) ? kKernelNames[kernel_id] : "";
 }
 
 }  // extern "C"

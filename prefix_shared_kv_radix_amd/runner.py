@@ -113,6 +113,7 @@ class Engine:
         self.on_decode = on_decode
         self.min_members = min_members
         self.content = np.full(workload.pool_slots, -1, np.int64)   # harness bookkeeping
+        self.row_stride = max(len(r.tokens) + len(r.out_tokens) for r in workload.requests)
         self.dirty = []
         self.dev = None
         if device is not None:
@@ -129,16 +130,13 @@ class Engine:
             while waiting:
                 order = self.tree.sched_order([w.requests[r].tokens for r in waiting], ph.policy)
                 waiting = [waiting[i] for i in order]
-                adm: List[Admission] = []
-                for rid in waiting:
-                    if len(adm) >= ph.batch_limit:
-                        break
-                    toks = w.requests[rid].tokens
-                    try:
-                        m, row, node = self.tree.admit(toks)
-                    except _lib.NoMemory:
-                        break
-                    adm.append(Admission(rid, m, len(toks), row.copy(), node))
+                cand = waiting[:ph.batch_limit]
+                k, rows, pl, nodes = self.tree.admit_batch([w.requests[r].tokens for r in cand],
+                                                           ph.batch_limit, self.row_stride)
+                adm: List[Admission] = [
+                    Admission(rid, int(pl[i]), len(w.requests[rid].tokens),
+                              rows[i, :len(w.requests[rid].tokens)].copy(), int(nodes[i]))
+                    for i, rid in enumerate(cand[:k])]
                 if not adm:
                     raise RuntimeError(f"request {waiting[0]} cannot be admitted into an idle pool")
                 taken = {a.rid for a in adm}
@@ -174,11 +172,14 @@ class Engine:
                     self._device_decode(rnd, ph, s, slots)
                 elif self.dev is not None:
                     self.dirty.append(slots.copy())
+        seqs, rows = [], np.zeros((B, self.row_stride), np.int32)
         for b, a in enumerate(rnd.admissions):
             r = w.requests[a.rid]
-            toks = np.concatenate([r.tokens, r.out_tokens[:ph.n_decode]])
-            row = np.concatenate([a.row, rnd.decode_slots[:, b]])
-            rnd.already_cached[b] = self.tree.finish(toks, row, a.prefix_len, a.node)
+            seqs.append(np.concatenate([r.tokens, r.out_tokens[:ph.n_decode]]))
+            rows[b, :a.prompt_len] = a.row
+            rows[b, a.prompt_len:a.prompt_len + ph.n_decode] = rnd.decode_slots[:, b]
+        rnd.already_cached[:] = self.tree.finish_batch(seqs, rows, [a.prefix_len for a in rnd.admissions],
+                                                       [a.node for a in rnd.admissions])
 
     # ---------------------------------------------------------------- device
     def _flush_dirty(self):
