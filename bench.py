@@ -112,11 +112,9 @@ class Episode:
                 st["dout"] = torch.empty((B, s.num_q_heads, s.head_dim_v), dtype=d.q_dtype, device=dev)
                 st["slot_pin"] = torch.empty((2, n, B), dtype=torch.int32, pin_memory=True)
                 st["slot_dev"] = torch.empty((n, B), dtype=torch.int32, device=dev)
-                max_shared = 0
-                if use_plan and rnd.plan is not None:
-                    max_shared = rnd.plan.max_shared
+                plan = rnd.plan if use_plan else None
                 self.max_ws = max(self.max_ws, _lib.decode_workspace_size(
-                    d.shape, B, int(seq.max()), max_shared, splits))
+                    d.shape, B, int(seq.max()), plan, splits))
             self.staged.append(st)
         self.ws = torch.empty(max(self.max_ws // 4, 1), dtype=torch.float32, device=dev)
         self.rtt_pin = torch.empty((2, max_batch, self.stride), dtype=torch.int32, pin_memory=True)
@@ -307,7 +305,7 @@ def main():
     dom = max(kern, key=lambda n: kern[n][1])
     byt, flop = algorithmic(w, ep, dom)
     t_dom = kern[dom][1] / args.steps / 1e3          # seconds per episode in that kernel
-    if dom in ("extend_mfma",):
+    if dom in ("extend_mfma", "mla_decode"):   # dense bf16 contractions: MFMA-bound
         roof = {"bound": "mfma", "achieved": flop / t_dom / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     else:

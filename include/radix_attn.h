@@ -191,6 +191,8 @@ radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const 
  *                         CSR of members; seg_member_slot = the segment's rank
  *                         on that member's path (0 = nearest the root)
  *   req_num_shared[batch], req_private_start[batch]
+ *   req_order[batch]      batch indices, requests with the same root-most shared
+ *                         segment consecutive (then those without one)
  *   *num_segments, *num_member_entries, *max_members, *max_shared
  * RADIX_E_INVAL if a capacity is too small (the needed counts are still written
  * to *num_segments and *num_member_entries). cap_seg >= 2*batch and
@@ -202,8 +204,9 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
                                     int32_t *seg_end, int32_t *seg_member_off,
                                     int32_t *seg_members, int32_t *seg_member_slot,
                                     int32_t *req_num_shared, int32_t *req_private_start,
-                                    int32_t *num_segments, int32_t *num_member_entries,
-                                    int32_t *max_members, int32_t *max_shared);
+                                    int32_t *req_order, int32_t *num_segments,
+                                    int32_t *num_member_entries, int32_t *max_members,
+                                    int32_t *max_shared);
 
 /* ======================================================================
  * Device side (HIP, gfx950). All pointers below marked "dev" are device
@@ -237,9 +240,11 @@ typedef struct {
   const int32_t *seg_members, *seg_member_slot; /* dev [num_member_entries] */
   const int32_t *req_num_shared;                /* dev [batch] */
   const int32_t *req_private_start;             /* dev [batch] */
+  const int32_t *req_order;                     /* dev [batch] or NULL */
   int32_t max_members;                          /* host: largest member count */
   int32_t max_shared;                           /* host: largest req_num_shared */
   int32_t max_seg_len;                          /* host: longest segment in tokens */
+  int32_t min_private_start;                    /* host: smallest req_private_start */
 } radix_decode_plan;
 
 /* Shapes compiled into this library (anything else: RADIX_E_UNSUPPORTED):
@@ -258,10 +263,13 @@ radix_status radix_kv_store(const radix_attn_shape *shape, const radix_kv_buffer
                             const int32_t *slots, int64_t num_tokens, void *stream);
 
 /* Workspace bytes radix_attn_decode needs for `batch` requests of at most
- * `max_seq_len` tokens, at most `max_shared` shared segments each and `num_splits`
- * private splits (0 = the split count radix_attn_decode chooses itself). */
+ * `max_seq_len` tokens with `plan` (NULL = no shared segments; only its host
+ * fields num_segments, max_members, max_shared and max_seg_len are read) and
+ * `num_splits` private splits (0 = the count radix_attn_decode chooses itself).
+ * 0 bytes means the call needs no workspace. */
 radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int32_t batch,
-                                              int32_t max_seq_len, int32_t max_shared,
+                                              int32_t max_seq_len,
+                                              const radix_decode_plan *plan,
                                               int32_t num_splits, size_t *bytes);
 
 /* Extend attention (prefill of new tokens against each request's cached prefix).
@@ -290,9 +298,11 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
  * first req_to_token[row][seq_lens[b]-1] = new_slots[b] and the new K/V row
  * (k_new/v_new/scale_new dev [batch, Hkv, *]) is stored at that slot.
  * With a plan, each shared segment's keys are read once for all its members and
- * keys from req_private_start[b] on are read per request, split into
- * `num_splits` chunks (0 = choose); all partial results are merged exactly by
- * their log-sum-exp. Without a plan (NULL) every request reads all its keys.
+ * keys from req_private_start[b] on are read per request; without a plan (NULL)
+ * every request reads all its keys. A request's private keys are cut into
+ * `num_splits` equal chunks of a common length (0 = choose: one chunk when the
+ * tails are short and the batch fills the GPU, else 512-key chunks); all partial
+ * results are merged exactly by their log-sum-exp.
  *   q dev [batch, Hq, Dqk]; out dev [batch, Hq, Dv]; lse_out dev [batch, Hq] or NULL;
  *   workspace dev, at least radix_attn_decode_workspace_size bytes.
  *   max_seq_len: host bound on seq_lens (grid sizing). */

@@ -9,12 +9,14 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import sys
 from dataclasses import dataclass
 
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libradix_attn.so")
+# RADIX_ATTN_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("RADIX_ATTN_LIB") or os.path.join(_HERE, "libradix_attn.so")
 
 OK, E_INVAL, E_NOMEM, E_HIP, E_UNSUPPORTED = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3 = 0, 1, 2
@@ -54,8 +56,9 @@ class DecodePlan(C.Structure):
     _fields_ = [("num_segments", C.c_int32), ("num_member_entries", C.c_int32),
                 ("seg_row", _vp), ("seg_start", _vp), ("seg_end", _vp), ("seg_member_off", _vp),
                 ("seg_members", _vp), ("seg_member_slot", _vp), ("req_num_shared", _vp),
-                ("req_private_start", _vp), ("max_members", C.c_int32), ("max_shared", C.c_int32),
-                ("max_seg_len", C.c_int32)]
+                ("req_private_start", _vp), ("req_order", _vp), ("max_members", C.c_int32),
+                ("max_shared", C.c_int32),
+                ("max_seg_len", C.c_int32), ("min_private_start", C.c_int32)]
 
 
 _SIGS = {
@@ -90,12 +93,13 @@ _SIGS = {
     "radix_kernel_name": (C.c_char_p, [C.c_int32]),
     "radix_tree_decode_plan": (C.c_int, [_vp, _i64p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                          _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
-                                         _i32p, _i32p, _i32p, _i32p]),
+                                         _i32p, _i32p, _i32p, _i32p, _i32p]),
     "radix_attn_supported": (C.c_int, [C.POINTER(AttnShape), C.c_int]),
     "radix_kv_store": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp, _vp, _vp,
                                  C.c_int64, _vp]),
     "radix_attn_decode_workspace_size": (C.c_int, [C.POINTER(AttnShape), C.c_int32, C.c_int32,
-                                                   C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]),
+                                                   C.POINTER(DecodePlan), C.c_int32,
+                                                   C.POINTER(C.c_size_t)]),
     "radix_attn_extend": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp, _vp, _vp,
                                     _vp, C.c_int32, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                     C.c_int32, _vp, _vp, _vp]),
@@ -152,9 +156,9 @@ class KVPool:
         self.h = h
 
     def close(self):
-        if self.h:
+        if self.h and not sys.is_finalizing():
             load().radix_kv_pool_destroy(self.h)
-            self.h = None
+        self.h = None
 
     __del__ = close
 
@@ -189,9 +193,9 @@ class RadixTree:
         self.pool = pool
 
     def close(self):
-        if self.h:
+        if self.h and not sys.is_finalizing():
             load().radix_tree_destroy(self.h)
-            self.h = None
+        self.h = None
 
     __del__ = close
 
@@ -316,7 +320,7 @@ class RadixTree:
         while True:
             seg = [np.zeros(cap_seg + (1 if k == 3 else 0), np.int32) for k in range(4)]
             mem = [np.zeros(cap_mem, np.int32) for _ in range(2)]
-            req = [np.zeros(max(B, 1), np.int32) for _ in range(2)]
+            req = [np.zeros(max(B, 1), np.int32) for _ in range(3)]
             cnt = [C.c_int32() for _ in range(4)]
             st = load().radix_tree_decode_plan(
                 self.h, nodes.ctypes.data_as(_i64p), B, int(min_members), cap_seg, cap_mem,
@@ -332,7 +336,7 @@ class RadixTree:
                         seg_member_off=seg[3][:ns + 1] if ns else np.zeros(1, np.int32),
                         seg_members=mem[0][:nm], seg_member_slot=mem[1][:nm],
                         req_num_shared=req[0][:B], req_private_start=req[1][:B],
-                        max_members=cnt[2].value, max_shared=cnt[3].value)
+                        req_order=req[2][:B], max_members=cnt[2].value, max_shared=cnt[3].value)
 
 
 @dataclass
@@ -345,12 +349,17 @@ class HostPlan:
     seg_member_slot: np.ndarray
     req_num_shared: np.ndarray
     req_private_start: np.ndarray
+    req_order: np.ndarray
     max_members: int
     max_shared: int
 
     @property
     def num_segments(self):
         return len(self.seg_row)
+
+    @property
+    def min_private_start(self):
+        return int(self.req_private_start.min()) if len(self.req_private_start) else 0
 
     @property
     def max_seg_len(self):
@@ -388,10 +397,23 @@ def kv_store(shape, kv, k_new, v_new, scale_new, slots, stream=None):
                                  _ptr(scale_new), _ptr(slots), int(slots.numel()), _stream(stream)))
 
 
-def decode_workspace_size(shape, batch, max_seq_len, max_shared, num_splits) -> int:
+def host_plan_struct(plan):
+    """DecodePlan carrying only the host scalars of a HostPlan (for workspace queries)."""
+    if plan is None or plan.num_segments == 0:
+        return None
+    return DecodePlan(plan.num_segments, len(plan.seg_members), None, None, None, None, None, None,
+                      None, None, None, plan.max_members, plan.max_shared, plan.max_seg_len,
+                      plan.min_private_start)
+
+
+def decode_workspace_size(shape, batch, max_seq_len, plan, num_splits) -> int:
+    """plan: a HostPlan, a DecodePlan or None."""
+    if isinstance(plan, HostPlan):
+        plan = host_plan_struct(plan)
     n = C.c_size_t()
     _check(load().radix_attn_decode_workspace_size(C.byref(shape), int(batch), int(max_seq_len),
-                                                   int(max_shared), int(num_splits), C.byref(n)))
+                                                   None if plan is None else C.byref(plan),
+                                                   int(num_splits), C.byref(n)))
     return n.value
 
 
@@ -412,9 +434,9 @@ def device_plan(plan: HostPlan, device):
         return None, []
     ts = [torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in
           (plan.seg_row, plan.seg_start, plan.seg_end, plan.seg_member_off, plan.seg_members,
-           plan.seg_member_slot, plan.req_num_shared, plan.req_private_start)]
+           plan.seg_member_slot, plan.req_num_shared, plan.req_private_start, plan.req_order)]
     dp = DecodePlan(plan.num_segments, len(plan.seg_members), *[_vp(t.data_ptr()) for t in ts],
-                    plan.max_members, plan.max_shared, plan.max_seg_len)
+                    plan.max_members, plan.max_shared, plan.max_seg_len, plan.min_private_start)
     return dp, ts
 
 

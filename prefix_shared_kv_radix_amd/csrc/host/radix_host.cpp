@@ -549,13 +549,15 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
                                     int32_t *seg_end, int32_t *seg_member_off,
                                     int32_t *seg_members, int32_t *seg_member_slot,
                                     int32_t *req_num_shared, int32_t *req_private_start,
-                                    int32_t *num_segments, int32_t *num_member_entries,
-                                    int32_t *max_members, int32_t *max_shared) {
+                                    int32_t *req_order, int32_t *num_segments,
+                                    int32_t *num_member_entries, int32_t *max_members,
+                                    int32_t *max_shared) {
   RADIX_REQUIRE(tree && batch >= 0 && (batch == 0 || nodes) && min_members >= 2,
                 "bad arguments");
   RADIX_REQUIRE(num_segments && num_member_entries && max_members && max_shared,
                 "null output pointer");
-  RADIX_REQUIRE(batch == 0 || (req_num_shared && req_private_start), "null output pointer");
+  RADIX_REQUIRE(batch == 0 || (req_num_shared && req_private_start && req_order),
+                "null output pointer");
   const RadixTree &t = tree->t;
   // paths (root first) and the number of running requests on each node
   std::vector<std::vector<int32_t>> paths(static_cast<size_t>(batch));
@@ -608,6 +610,20 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
     req_num_shared[b] = rank;
     req_private_start[b] = static_cast<int32_t>(priv);
     maxsh = std::max(maxsh, rank);
+  }
+  // requests grouped by their root-most shared segment (segment creation order), then
+  // the requests without any, in batch order
+  {
+    int32_t k = 0;
+    std::vector<uint8_t> placed(static_cast<size_t>(batch), 0);
+    for (const auto &sg : segs)
+      for (const auto &m : sg.members)
+        if (m.second == 0 && !placed[m.first]) {
+          placed[m.first] = 1;
+          req_order[k++] = m.first;
+        }
+    for (int32_t b = 0; b < batch; ++b)
+      if (!placed[b]) req_order[k++] = b;
   }
   *num_segments = static_cast<int32_t>(segs.size());
   *num_member_entries = total_mem;

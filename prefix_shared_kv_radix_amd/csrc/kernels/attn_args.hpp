@@ -36,7 +36,15 @@ struct AttnArgs {
   const int32_t *seg_row, *seg_start, *seg_end, *seg_member_off, *seg_members, *seg_member_slot;
   int num_segments;
   const int32_t *req_num_shared;
-  int num_splits, parts, part_base;
+  int num_splits;   // private splits per request
+  int split_chunk;  // keys per private split (all requests), when num_splits > 1
+  int seg_splits;   // key splits per shared segment
+  int parts, part_base;  // partial slots per (request, head); private ones start at part_base
+  // decode: the new token's K/V (read directly for the last position and stored by the
+  // tail kernel) and its slot (appended to the slot list); all NULL when already stored
+  const void *k_new, *v_new;
+  const int32_t *new_slots;
+  int32_t *rtt_mut;
   void *out;
   float *lse;
   float *ws_o, *ws_lse;
@@ -44,8 +52,27 @@ struct AttnArgs {
   float scale_log2;
 };
 
+struct MlaArgs {
+  const uint16_t *q;       // [batch, 128, 576] bf16
+  const void *kv;          // [slots, 576] bf16, or E4M3 bytes
+  const float *kv_scale;   // [slots] (fp8)
+  const int32_t *rtt;
+  int rtt_stride;
+  const int32_t *req_rows;
+  const int32_t *seq_lens;
+  const int32_t *req_order;  // [batch] or NULL: requests sharing a prefix are consecutive
+  int batch, nsplit, split_chunk, parts;
+  float *ws_o, *ws_lse;      // partials when nsplit > 1
+  uint16_t *out;             // [batch, 128, 512] bf16 when nsplit == 1
+  float *lse;
+  float scale_log2;
+  int fp8;
+};
+
 hipError_t kv_store(const StoreArgs &a, int64_t T, hipStream_t stream);
-// mode 0: decode private tail (split-KV), 1: extend (one block per token), 2: shared segment
+hipError_t mla(const MlaArgs &a, hipStream_t s);
+// mode 0: decode private tail split -> partial, 1: extend (one block per token),
+// 2: shared segment -> partial, 3: decode private tail -> final output (merges shared partials)
 hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, unsigned splits,
                 hipStream_t s);
 hipError_t mfma(int G, bool seg, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s);

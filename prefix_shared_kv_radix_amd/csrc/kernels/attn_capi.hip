@@ -93,6 +93,8 @@ AttnArgs attn_args(const radix_attn_shape *s, const radix_kv_buffers *kv, const 
   a.Hq = s->num_q_heads;
   a.Hkv = s->num_kv_heads;
   a.scale_log2 = s->sm_scale * kLog2e;
+  a.num_splits = 1;
+  a.seg_splits = 1;
   return a;
 }
 
@@ -136,25 +138,54 @@ struct Timed {
   }
 };
 
-int auto_splits(int batch, int hkv, int max_seq_len) {
-  const int target = 2048;  // resident blocks to fill 256 CUs several times over
-  int s = (target + batch * hkv - 1) / (batch * hkv > 0 ? batch * hkv : 1);
-  const int cap = max_seq_len / 256 > 1 ? max_seq_len / 256 : 1;
-  if (s > cap) s = cap;
-  if (s > 32) s = 32;
+// Key splits per shared segment: enough blocks to fill the chip (~512 for the MFMA
+// segment kernel), at least 256 keys per split, at most 16 splits.
+int seg_splits_for(const radix_attn_shape *s, const radix_decode_plan *plan) {
+  if (!plan || plan->num_segments <= 0) return 1;
+  const bool mla = s->v_is_k_prefix != 0;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const long rows = static_cast<long>(plan->max_members) * (mla ? 1 : G);
+  const long tiles = mla ? rows : (rows + 127) / 128;
+  const long blocks = tiles * plan->num_segments * s->num_kv_heads;
+  const long target = mla ? 1024 : 512;
+  long ss = (target + blocks - 1) / (blocks > 0 ? blocks : 1);
+  const long cap = plan->max_seg_len / 256 > 1 ? plan->max_seg_len / 256 : 1;
+  if (ss > cap) ss = cap;
+  if (ss > 16) ss = 16;
+  return ss < 1 ? 1 : static_cast<int>(ss);
+}
+
+// Private-tail chunking: one chunk per request when the tails are short and the batch
+// alone gives ~2048 waves; otherwise 512-key chunks (more for very long tails), so
+// requests of very different lengths still spread evenly over the GPU.
+constexpr int kTailChunk = 512;
+int auto_splits(int batch, int hkv, int private_len) {
+  if (private_len <= 2 * kTailChunk && batch * hkv >= 2048) return 1;
+  int s = (private_len + kTailChunk - 1) / kTailChunk;
+  if (s > 64) s = 64;
   return s < 1 ? 1 : s;
+}
+
+// MLA: one block per request and key chunk, 4 waves; enough chunks for >= 256 blocks,
+// at least 512 keys per chunk.
+int mla_splits(int batch, int max_seq_len) {
+  int s = (256 + batch - 1) / (batch > 0 ? batch : 1);
+  const int cap = max_seq_len / 512 > 1 ? max_seq_len / 512 : 1;
+  if (s > cap) s = cap;
+  return s < 1 ? 1 : s;
+}
+
+int private_len_bound(int max_seq_len, const radix_decode_plan *plan) {
+  const bool use_plan = plan && plan->num_segments > 0;
+  const int p = max_seq_len - (use_plan ? plan->min_private_start : 0);
+  return p < 1 ? 1 : p;
 }
 
 }  // namespace
 
 extern "C" {
 
-radix_status radix_mla_decode_impl(const radix_attn_shape *shape, const radix_kv_buffers *kv,
-                                   const void *q, const int32_t *rtt, int32_t stride,
-                                   const int32_t *rows, const int32_t *seq_lens, int32_t batch,
-                                   int32_t max_seq_len, const radix_decode_plan *plan,
-                                   int32_t num_splits, void *out, float *lse, float *ws_o,
-                                   float *ws_lse, int32_t parts, hipStream_t stream);
+
 
 radix_status radix_attn_supported(const radix_attn_shape *shape, int is_decode) {
   Kind k = classify(shape);
@@ -189,12 +220,29 @@ radix_status radix_kv_store(const radix_attn_shape *shape, const radix_kv_buffer
 }
 
 radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int32_t batch,
-                                              int32_t max_seq_len, int32_t max_shared,
+                                              int32_t max_seq_len,
+                                              const radix_decode_plan *plan,
                                               int32_t num_splits, size_t *bytes) {
-  REQUIRE(shape && bytes && batch >= 0 && max_seq_len >= 0 && max_shared >= 0 && num_splits >= 0,
+  REQUIRE(shape && bytes && batch >= 0 && max_seq_len >= 0 && num_splits >= 0,
           "bad workspace query");
-  if (num_splits == 0) num_splits = auto_splits(batch, shape->num_kv_heads, max_seq_len);
-  const size_t parts = static_cast<size_t>(max_shared) + static_cast<size_t>(num_splits);
+  if (shape->v_is_k_prefix) {  // MLA: partials only when a request's keys are split
+    const int ns = num_splits > 0 ? num_splits : mla_splits(batch, max_seq_len);
+    *bytes = ns == 1 ? 0
+                     : static_cast<size_t>(batch) * shape->num_q_heads * ns *
+                           (static_cast<size_t>(shape->head_dim_v) + 1) * sizeof(float);
+    return RADIX_OK;
+  }
+  if (num_splits == 0)
+    num_splits = auto_splits(batch, shape->num_kv_heads, private_len_bound(max_seq_len, plan));
+  const bool use_plan = plan && plan->num_segments > 0;
+  const size_t shared = use_plan ? static_cast<size_t>(plan->max_shared) *
+                                       static_cast<size_t>(seg_splits_for(shape, plan))
+                                 : 0;
+  const size_t parts = shared + static_cast<size_t>(num_splits);
+  if (!use_plan && num_splits == 1) {
+    *bytes = 0;  // single pass, nothing to merge
+    return RADIX_OK;
+  }
   *bytes = static_cast<size_t>(batch) * shape->num_q_heads * parts *
            (static_cast<size_t>(shape->head_dim_v) + 1) * sizeof(float);
   return RADIX_OK;
@@ -270,46 +318,93 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
                 plan->max_members > 0 && plan->max_shared > 0,
             "incomplete decode plan");
   }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Kind kind = classify(shape);
+  if (kind == Kind::MlaBf16 || kind == Kind::MlaFp8) {
+    const int nsplit = num_splits > 0 ? num_splits : mla_splits(batch, max_seq_len);
+    size_t need = 0;
+    radix_attn_decode_workspace_size(shape, batch, max_seq_len, plan, nsplit, &need);
+    REQUIRE(nsplit == 1 || (workspace && workspace_bytes >= need), "decode workspace too small");
+    REQUIRE(!use_plan || plan->req_order, "decode plan without req_order");
+    if (k_new) {  // the MLA kernel reads every key from the pool: store the new row first
+      StoreArgs sa = store_args(shape, kv, k_new, v_new, scale_new);
+      sa.new_slots = new_slots;
+      sa.rtt = req_to_token;
+      sa.rtt_stride = rtt_stride;
+      sa.req_rows = req_rows;
+      sa.seq_lens = seq_lens;
+      sa.mode = new_slots ? 1 : 3;
+      Timed t(K_STORE, s);
+      st = hip_status(radix_launch::kv_store(sa, batch, s), "kv_store launch");
+      if (st != RADIX_OK) return st;
+    }
+    radix_launch::MlaArgs m{};
+    m.q = static_cast<const uint16_t *>(q);
+    m.kv = kv->k_pool;
+    m.kv_scale = kv->kv_scale;
+    m.rtt = req_to_token;
+    m.rtt_stride = rtt_stride;
+    m.req_rows = req_rows;
+    m.seq_lens = seq_lens;
+    m.req_order = use_plan ? plan->req_order : nullptr;
+    m.batch = batch;
+    m.nsplit = nsplit;
+    m.split_chunk = ((max_seq_len + nsplit - 1) / nsplit + 31) / 32 * 32;
+    m.parts = nsplit;
+    m.ws_o = nsplit > 1 ? static_cast<float *>(workspace) : nullptr;
+    m.ws_lse = nsplit > 1 ? m.ws_o + static_cast<size_t>(batch) * shape->num_q_heads * nsplit *
+                                         shape->head_dim_v
+                          : nullptr;
+    m.out = static_cast<uint16_t *>(out);
+    m.lse = lse_out;
+    m.scale_log2 = shape->sm_scale * kLog2e;
+    m.fp8 = kind == Kind::MlaFp8;
+    {
+      Timed t(K_MLA_DECODE, s);
+      st = hip_status(radix_launch::mla(m, s), "mla launch");
+    }
+    if (st != RADIX_OK || nsplit == 1) return st;
+    AttnArgs c = attn_args(shape, kv, q, req_to_token, rtt_stride, req_rows, out, lse_out);
+    c.num_splits = nsplit;
+    c.parts = nsplit;
+    c.part_base = 0;
+    c.ws_o = m.ws_o;
+    c.ws_lse = m.ws_lse;
+    Timed t(K_MLA_COMBINE, s);
+    return hip_status(radix_launch::combine(true, c, batch, shape->head_dim_v, s), "combine launch");
+  }
+
   const int splits = num_splits > 0 ? num_splits
-                                    : auto_splits(batch, shape->num_kv_heads, max_seq_len);
-  const int max_shared = use_plan ? plan->max_shared : 0;
+                                    : auto_splits(batch, shape->num_kv_heads,
+                                                  private_len_bound(max_seq_len, plan));
+  const int seg_splits = use_plan ? seg_splits_for(shape, plan) : 1;
+  const int max_shared = use_plan ? plan->max_shared * seg_splits : 0;
   const int parts = max_shared + splits;
   const bool direct = !use_plan && splits == 1;
   size_t need = 0;
-  radix_attn_decode_workspace_size(shape, batch, max_seq_len, max_shared, splits, &need);
+  radix_attn_decode_workspace_size(shape, batch, max_seq_len, plan, splits, &need);
   REQUIRE(direct || (workspace && workspace_bytes >= need), "decode workspace too small");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  if (k_new) {
-    StoreArgs sa = store_args(shape, kv, k_new, v_new, scale_new);
-    sa.new_slots = new_slots;
-    sa.rtt = req_to_token;
-    sa.rtt_stride = rtt_stride;
-    sa.req_rows = req_rows;
-    sa.seq_lens = seq_lens;
-    sa.mode = new_slots ? 1 : 3;
-    Timed t(K_STORE, s);
-    st = hip_status(radix_launch::kv_store(sa, batch, s), "kv_store launch");
-    if (st != RADIX_OK) return st;
-  }
-
   float *ws_o = direct ? nullptr : static_cast<float *>(workspace);
   float *ws_lse = direct ? nullptr
                          : ws_o + static_cast<size_t>(batch) * shape->num_q_heads * parts *
                                       shape->head_dim_v;
-  const Kind kind = classify(shape);
-  if (kind == Kind::MlaBf16 || kind == Kind::MlaFp8)
-    return radix_mla_decode_impl(shape, kv, q, req_to_token, rtt_stride, req_rows, seq_lens,
-                                 batch, max_seq_len, use_plan ? plan : nullptr, splits, out,
-                                 lse_out, ws_o, ws_lse, parts, s);
 
   AttnArgs a = attn_args(shape, kv, q, req_to_token, rtt_stride, req_rows, out, lse_out);
   a.seq_lens = seq_lens;
   a.num_splits = splits;
+  {
+    const int plen = private_len_bound(max_seq_len, use_plan ? plan : nullptr);
+    a.split_chunk = ((plen + splits - 1) / splits + 15) & ~15;
+  }
+  a.seg_splits = seg_splits;
   a.parts = parts;
   a.part_base = max_shared;
   a.ws_o = ws_o;
   a.ws_lse = ws_lse;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_slots = new_slots;
+  a.rtt_mut = req_to_token;
   const bool bf16 = kind == Kind::GqaBf16;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (use_plan) {
@@ -324,20 +419,25 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     a.private_start = plan->req_private_start;
     if (bf16) {
       Timed t(K_SEGMENT_MFMA, s);
-      st = hip_status(radix_launch::mfma(G, true, a, plan->max_members * G, plan->num_segments, s),
+      st = hip_status(radix_launch::mfma(G, true, a, plan->max_members * G,
+                                         static_cast<unsigned>(plan->num_segments * seg_splits), s),
                       "segment launch");
     } else {
       Timed t(K_SEGMENT_VALU, s);
-      st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, 1, s),
+      st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, seg_splits, s),
                       "segment launch");
     }
     if (st != RADIX_OK) return st;
+  }
+  if (splits == 1) {
+    Timed t(K_DECODE_TAIL, s);
+    return hip_status(radix_launch::valu(bf16, G, 3, a, batch, 1, s), "decode launch");
   }
   {
     Timed t(K_DECODE_TAIL, s);
     st = hip_status(radix_launch::valu(bf16, G, 0, a, batch, splits, s), "decode launch");
   }
-  if (st != RADIX_OK || direct) return st;
+  if (st != RADIX_OK) return st;
   Timed t(K_COMBINE, s);
   return hip_status(radix_launch::combine(bf16, a, batch, shape->head_dim_v, s), "combine launch");
 }

@@ -34,6 +34,11 @@ using radix_launch::StoreArgs;
 
 namespace {
 
+#ifndef RADIX_VALU_STAGES
+#define RADIX_VALU_STAGES 3
+#endif
+constexpr int kValuStages = RADIX_VALU_STAGES;  // register buffers in the VALU kernel's ring
+
 __device__ __forceinline__ int find_owner(const int32_t *off, int n, int t) {
   // largest i in [0, n) with off[i] <= t
   int lo = 0, hi = n - 1;
@@ -116,27 +121,47 @@ template <> __device__ __forceinline__ void store_out<uint16_t>(void *out, int64
   reinterpret_cast<uint16_t *>(out)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
 }
 
-// MODE 0: decode private tail (per request, split-KV)
-// MODE 1: extend, one block per new token
-// MODE 2: decode shared segment, one block per (segment, member) entry
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ mask) << 2,
+                                                                 __builtin_bit_cast(int, x)));
+}
+
+// One wave = one query token (the G query heads of one KV head) against one key range.
+// 16 lanes cover a 256-byte K (or V) row with 16-byte loads, so a wave takes 4 rows per
+// load and 16 rows per iteration; the next iteration's slot indices and K/V rows are in
+// flight while the current one is computed. The four 16-lane groups (different rows,
+// same dims) are merged with cross-lane exchanges at the end; no LDS, no barriers.
+// Work item w = blockIdx.x * 4 + wave, decomposed as ((item * nsplit + split) * Hkv + kvh).
+// MODE 0: decode private tail, one of several splits -> partial (o, lse) in the workspace
+// MODE 1: extend (fp32 path), item = new token -> final output
+// MODE 2: decode shared segment (fp32 path), item = (segment, member) entry -> partial
+// MODE 3: decode private tail, single split -> final output, merged with the request's
+//         shared-segment partials (written earlier on the same stream)
+// In MODE 0 and 3 the newest key (position seq_len-1) is read from k_new/v_new when given,
+// and the split-0 wave stores it into the pool and appends its slot to the slot list.
 template <typename T, int D, int G, int MODE>
-__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int n_items, int nsplit) {
   constexpr int EPL = Vec16<T>::N;
   static_assert(D / EPL == 16, "16 lanes per row");
-  const int item = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, sub = lane & 15;
+  constexpr bool TAIL = MODE == 0 || MODE == 3;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+  const int w = blockIdx.x * 4 + wave;
+  if (w >= n_items * nsplit * a.Hkv) return;
+  const int kvh = w % a.Hkv;
+  const int split = (w / a.Hkv) % nsplit;
+  const int item = w / (a.Hkv * nsplit);
 
   int b, lo, hi, part = 0;
   int64_t q_row;
   const int32_t *rtt_row;
   if (MODE == 1) {
     b = find_owner(a.cu_extend, a.batch, item);
-    int i = item - a.cu_extend[b];
+    const int i = item - a.cu_extend[b];
     lo = 0;
     hi = a.prefix_lens[b] + i + 1;
     q_row = item;
     rtt_row = rtt_row_of(a, b);
-  } else if (MODE == 0) {
+  } else if (TAIL) {
     b = item;
     hi = a.seq_lens[b];
     lo = a.private_start ? a.private_start[b] : 0;
@@ -144,27 +169,47 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     rtt_row = rtt_row_of(a, b);
     part = a.part_base + split;
   } else {
-    int s = find_owner(a.seg_member_off, a.num_segments, item);
+    const int sg = find_owner(a.seg_member_off, a.num_segments, item);
     b = a.seg_members[item];
-    lo = a.seg_start[s];
-    hi = a.seg_end[s];
+    lo = a.seg_start[sg];
+    hi = a.seg_end[sg];
     q_row = b;
-    rtt_row = rtt_row_of(a, a.seg_row[s]);
-    part = a.seg_member_slot[item];
+    rtt_row = rtt_row_of(a, a.seg_row[sg]);
+    part = a.seg_member_slot[item] * a.seg_splits + split;
   }
-  const int n = hi - lo;
-  const int nsplit = static_cast<int>(gridDim.z);
-  const int chunk = ((n + nsplit - 1) / nsplit + 63) & ~63;
+  // TAIL: common chunk length (a.split_chunk) so uneven requests spread evenly;
+  // MODE 2: the segment's own length cut into nsplit pieces
+  const int chunk = (TAIL && nsplit > 1) ? a.split_chunk : ((hi - lo + nsplit - 1) / nsplit + 15) & ~15;
   const int s_lo = lo + split * chunk;
   const int s_hi = min(hi, s_lo + chunk);
 
+  const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * D * sizeof(T);
+  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * D * sizeof(T) + sub * 16;
+  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * sizeof(T) + sub * 16;
+  const bool fuse_new = TAIL && a.k_new != nullptr;
+  const char *knew = nullptr, *vnew = nullptr;
+  if (fuse_new) {
+    const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D * sizeof(T) + sub * 16;
+    knew = reinterpret_cast<const char *>(a.k_new) + off;
+    vnew = reinterpret_cast<const char *>(a.v_new) + off;
+    if (split == 0 && grp == 0) {
+      const int64_t at = static_cast<int64_t>(a.req_rows ? a.req_rows[b] : b) * a.rtt_stride + hi - 1;
+      const int64_t slot = a.new_slots ? a.new_slots[b] : a.rtt[at];
+      if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[at] = static_cast<int32_t>(slot);
+      *reinterpret_cast<u32x4 *>(const_cast<char *>(kb) + slot * row_bytes) = ldg16(knew);
+      *reinterpret_cast<u32x4 *>(const_cast<char *>(vb) + slot * row_bytes) = ldg16(vnew);
+    }
+  }
+
   float qf[G][EPL];
-  const T *qp = reinterpret_cast<const T *>(a.q) + (q_row * a.Hq + kvh * G) * D + sub * EPL;
+  {
+    const T *qp = reinterpret_cast<const T *>(a.q) + (q_row * a.Hq + kvh * G) * D + sub * EPL;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    Vec16<T>::unpack(ldg16(qp + h * D), qf[h]);
+    for (int h = 0; h < G; ++h) {
+      Vec16<T>::unpack(ldg16(qp + h * D), qf[h]);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[h][e] *= a.scale_log2;
+      for (int e = 0; e < EPL; ++e) qf[h][e] *= a.scale_log2;
+    }
   }
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -174,103 +219,169 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-  const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * D * sizeof(T);
-  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * D * sizeof(T) + sub * 16;
-  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * sizeof(T) + sub * 16;
 
-  for (int base = s_lo + wave * 16; base < s_hi; base += 64) {
-    u32x4 kr[4], vr[4];
-    bool valid[4];
+  // ring of NB register buffers: iteration t (16 rows) is computed while the K/V rows of
+  // iterations t+1 .. t+NB-1 and the slot indices of iteration t+NB are in flight
+  constexpr int NB = kValuStages;
+  u32x4 kbuf[NB][4], vbuf[NB][4];
+  int32_t sbuf[NB][4];
+  // Loads are unconditional (no branches around them, so the compiler can count the
+  // loads in flight): rows past the range read a clamped slot-list entry / slot 0 and
+  // are masked after the load.
+  const int last = s_hi - 1;   // >= 0: s_hi >= 1 always
+  auto load_slots = [&](int base, int32_t *sl) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      int r = base + u * 4 + grp;
-      valid[u] = r < s_hi;
-      kr[u] = u32x4{0, 0, 0, 0};
-      vr[u] = u32x4{0, 0, 0, 0};
-      if (valid[u]) {
-        int64_t slot = rtt_row[r];
-        kr[u] = ldg16(kb + slot * row_bytes);
-        vr[u] = ldg16(vb + slot * row_bytes);
-      }
+      const int r = base + u * 4 + grp;
+      const int32_t v = rtt_row[min(r, last)];
+      sl[u] = (r < s_hi && !(fuse_new && r == hi - 1)) ? v : 0;
     }
-    float s[4][G];
+  };
+  auto load_kv = [&](int base, const int32_t *sl, u32x4 *kd, u32x4 *vd) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = base + u * 4 + grp;
+      const bool newest = fuse_new && r == hi - 1;
+      const char *kp = newest ? knew : kb + static_cast<int64_t>(sl[u]) * row_bytes;
+      const char *vp = newest ? vnew : vb + static_cast<int64_t>(sl[u]) * row_bytes;
+      kd[u] = ldg16(kp);
+      vd[u] = ldg16(vp);
+    }
+  };
+  auto compute = [&](int base, const u32x4 *kr, const u32x4 *vr) {
+    float p[4][G];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       float kf[EPL];
       Vec16<T>::unpack(kr[u], kf);
+      const bool valid = base + u * 4 + grp < s_hi;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) d = fmaf(qf[h][e], kf[e], d);
         d = sum16(d);
-        s[u][h] = valid[u] ? d : -INFINITY;
+        p[u][h] = valid ? d : -INFINITY;
       }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-      float mn = fmaxf(m[h], mx);
-      float alpha = exp2f(m[h] - mn);
-      float p[4];
+      const float mx = fmaxf(fmaxf(p[0][h], p[1][h]), fmaxf(p[2][h], p[3][h]));
+      const float mn = fmaxf(m[h], mx);
+      const float alpha = exp2f(m[h] - mn);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) p[u] = exp2f(s[u][h] - mn);
-      l[h] = l[h] * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+      for (int u = 0; u < 4; ++u) p[u][h] = exp2f(p[u][h] - mn);
+      l[h] = l[h] * alpha + ((p[0][h] + p[1][h]) + (p[2][h] + p[3][h]));
       m[h] = mn;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const bool valid = base + u * 4 + grp < s_hi;
+      u32x4 w = vr[u];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = valid ? w[c] : 0u;   // masked rows may hold NaN
       float vf[EPL];
-      Vec16<T>::unpack(vr[u], vf);
+      Vec16<T>::unpack(w, vf);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float p = exp2f(s[u][h] - m[h]);
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-      }
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p[u][h], vf[e], acc[h][e]);
+    }
+  };
+
+  // Step t computes iteration t (buffer t % NB). Before that it issues, in this order,
+  // the slot indices of iteration t+NB and the K/V rows of iteration t+NB-1 (whose slots
+  // came one step earlier). Loads return in issue order, so waiting for those slots
+  // never waits for the K/V rows issued one step earlier: NB-1 iterations stay in flight.
+#pragma unroll
+  for (int j = 0; j < NB; ++j) load_slots(s_lo + 16 * j, sbuf[j]);
+#pragma unroll
+  for (int j = 0; j + 1 < NB; ++j) load_kv(s_lo + 16 * j, sbuf[j], kbuf[j], vbuf[j]);
+  for (int base = s_lo; base < s_hi; base += 16 * NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int it = base + 16 * j;
+      if (it >= s_hi) break;
+      const int jl = (j + NB - 1) % NB;
+      const int ahead = it + 16 * (NB - 1);
+      load_slots(ahead + 16, sbuf[j]);
+      load_kv(ahead, sbuf[jl], kbuf[jl], vbuf[jl]);
+      compute(it, kbuf[j], vbuf[j]);
     }
   }
 
-  // merge the 16 (wave, lane-group) states, one head at a time
-  __shared__ float sm_m[16], sm_l[16];
-  __shared__ float sm_acc[16][D];
-  const int st = wave * 4 + grp;
+  // merge the four 16-lane groups (same dims, other rows); afterwards every lane holds
+  // the wave's state for its 8 (bf16) or 4 (fp32) dims of every head
+#pragma unroll
+  for (int mask = 16; mask <= 32; mask <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = shfl_xor_f(m[h], mask), lo_ = shfl_xor_f(l[h], mask);
+      const float mn = fmaxf(m[h], mo);
+      const float wa = exp2f(m[h] - mn), wb = exp2f(mo - mn);
+      l[h] = l[h] * wa + lo_ * wb;
+      m[h] = mn;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * wa + shfl_xor_f(acc[h][e], mask) * wb;
+    }
+  }
+
+  // lane group g writes heads g, g+4, ...; dims sub*EPL .. sub*EPL+EPL-1
+  const int nshared = (MODE == 3 && a.req_num_shared) ? a.req_num_shared[b] * a.seg_splits : 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    if (sub == 0) {
-      sm_m[st] = m[h];
-      sm_l[st] = l[h];
-    }
+    if ((h & 3) != grp) continue;
+    const int head = kvh * G + h;
+    float M = m[h], L = l[h];
+    float O[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) sm_acc[st][sub * EPL + e] = acc[h][e];
-    __syncthreads();
-    for (int d = tid; d < D; d += 256) {
-      float M = kNegBig;
+    for (int e = 0; e < EPL; ++e) O[e] = acc[h][e];
+    if (MODE == 3) {
+      // shared-segment partials (o normalised, lse in log2 units), four at a time
+      const int64_t hp = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
+      for (int p0 = 0; p0 < nshared; p0 += 4) {
+        float pl[4];
+        f32x4 po[4][EPL / 4];
 #pragma unroll
-      for (int x = 0; x < 16; ++x) M = fmaxf(M, sm_m[x]);
-      float L = 0.f, O = 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = p0 + j < nshared;
+          pl[j] = ok ? a.ws_lse[hp + p0 + j] : -INFINITY;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float w = exp2f(sm_m[x] - M);
-        L = fmaf(sm_l[x], w, L);
-        O = fmaf(sm_acc[x][d], w, O);
+          for (int c = 0; c < EPL / 4; ++c)
+            po[j][c] = ok ? *reinterpret_cast<const f32x4 *>(a.ws_o + (hp + p0 + j) * D + sub * EPL + 4 * c)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float mn = fmaxf(M, pl[j]);
+          const float wa = exp2f(M - mn), wb = exp2f(pl[j] - mn);
+          L = L * wa + wb;
+          M = mn;
+#pragma unroll
+          for (int c = 0; c < EPL / 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[4 * c + e] = O[4 * c + e] * wa + po[j][c][e] * wb;
+        }
       }
-      const int head = kvh * G + h;
-      const bool empty = !(L > 0.f);
-      const float o = empty ? 0.f : O / L;
-      const float lse2 = empty ? -INFINITY : M + log2f(L);
-      if (MODE == 1 || (MODE == 0 && a.ws_o == nullptr)) {
-        store_out<T>(a.out, (q_row * a.Hq + head) * D + d, o);
-        if (a.lse && d == 0) a.lse[q_row * a.Hq + head] = lse2 * kLn2;
-      } else {
-        const int64_t pi = (static_cast<int64_t>(b) * a.Hq + head) * a.parts + part;
-        a.ws_o[pi * D + d] = o;
-        if (d == 0) a.ws_lse[pi] = lse2;
-      }
     }
-    __syncthreads();
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    const float lse2 = empty ? -INFINITY : M + log2f(L);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) O[e] *= inv;
+    if (MODE == 1 || MODE == 3) {
+      Vec16<T>::store(reinterpret_cast<T *>(a.out) + (q_row * a.Hq + head) * D + sub * EPL, O);
+      if (a.lse && sub == 0) a.lse[q_row * a.Hq + head] = lse2 * kLn2;
+    } else {
+      const int64_t pi = (static_cast<int64_t>(b) * a.Hq + head) * a.parts + part;
+#pragma unroll
+      for (int c = 0; c < EPL / 4; ++c)
+        *reinterpret_cast<f32x4 *>(a.ws_o + pi * D + sub * EPL + 4 * c) =
+            f32x4{O[4 * c], O[4 * c + 1], O[4 * c + 2], O[4 * c + 3]};
+      if (sub == 0) a.ws_lse[pi] = lse2;
+    }
   }
 }
 
@@ -303,12 +414,16 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     hi = P + i_last + 1;
     rtt_row = rtt_row_of(a, b);
   } else {
-    mem_off = a.seg_member_off[item];
-    nrows = (a.seg_member_off[item + 1] - mem_off) * G;
+    // blockIdx.y = segment * seg_splits + key split of that segment
+    const int sg = item / a.seg_splits, ks = item % a.seg_splits;
+    mem_off = a.seg_member_off[sg];
+    nrows = (a.seg_member_off[sg + 1] - mem_off) * G;
     if (tile * MF_BM >= nrows) return;
-    lo = a.seg_start[item];
-    hi = a.seg_end[item];
-    rtt_row = rtt_row_of(a, a.seg_row[item]);
+    const int s0 = a.seg_start[sg], s1 = a.seg_end[sg];
+    const int chunk = ((s1 - s0 + a.seg_splits - 1) / a.seg_splits + MF_BN - 1) / MF_BN * MF_BN;
+    lo = s0 + ks * chunk;
+    hi = min(s1, lo + chunk);
+    rtt_row = rtt_row_of(a, a.seg_row[sg]);
   }
 
   // this lane's query row
@@ -450,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       }
     if (a.lse && h == 0) a.lse[q_tok * a.Hq + head] = lse2 * kLn2;
   } else {
-    const int part = a.seg_member_slot[mem_off + qi];
+    const int part = a.seg_member_slot[mem_off + qi] * a.seg_splits + item % a.seg_splits;
     const int64_t pi = (q_tok * a.Hq + head) * a.parts + part;
     float *wp = a.ws_o + pi * MF_D;
 #pragma unroll
@@ -470,7 +585,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 template <typename T>
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a, int Dv) {
   const int b = blockIdx.x, head = blockIdx.y;
-  const int ns = a.req_num_shared ? a.req_num_shared[b] : 0;
+  const int ns = a.req_num_shared ? a.req_num_shared[b] * a.seg_splits : 0;
   const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
   float M = -INFINITY;
   for (int p = 0; p < ns; ++p) M = fmaxf(M, a.ws_lse[base + p]);
@@ -507,10 +622,14 @@ hipError_t kv_store(const StoreArgs &a, int64_t T, hipStream_t stream) {
 template <typename T, int D, int G>
 static hipError_t launch_valu(int mode, const AttnArgs &a, unsigned items, unsigned splits,
                               hipStream_t stream) {
-  dim3 grid(items, a.Hkv, splits), block(256);
-  if (mode == 0) attn_valu_kernel<T, D, G, 0><<<grid, block, 0, stream>>>(a);
-  else if (mode == 1) attn_valu_kernel<T, D, G, 1><<<grid, block, 0, stream>>>(a);
-  else attn_valu_kernel<T, D, G, 2><<<grid, block, 0, stream>>>(a);
+  const uint64_t waves = static_cast<uint64_t>(items) * splits * a.Hkv;
+  if (waves > 0x7fffffffull) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+  const int n = static_cast<int>(items), ns = static_cast<int>(splits);
+  if (mode == 0) attn_valu_kernel<T, D, G, 0><<<grid, block, 0, stream>>>(a, n, ns);
+  else if (mode == 1) attn_valu_kernel<T, D, G, 1><<<grid, block, 0, stream>>>(a, n, ns);
+  else if (mode == 2) attn_valu_kernel<T, D, G, 2><<<grid, block, 0, stream>>>(a, n, ns);
+  else attn_valu_kernel<T, D, G, 3><<<grid, block, 0, stream>>>(a, n, ns);
   return hipGetLastError();
 }
 

@@ -259,9 +259,8 @@ class Engine:
         v_new = None if d.v_tab is None else d.v_tab[rows]
         sc_new = None if d.sc_tab is None else d.sc_tab[rows]
         plan, _keep = self._plan_dev
-        max_shared = plan.max_shared if plan is not None else 0
         splits = self.num_splits or 0
-        ws_bytes = _lib.decode_workspace_size(d.shape, B, int(seq.max()), max_shared, splits)
+        ws_bytes = _lib.decode_workspace_size(d.shape, B, int(seq.max()), plan, splits)
         ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=d.device)
         out = torch.empty((B, s.num_q_heads, s.head_dim_v), dtype=d.q_dtype, device=d.device)
         lse = torch.empty((B, s.num_q_heads), dtype=torch.float32, device=d.device)
