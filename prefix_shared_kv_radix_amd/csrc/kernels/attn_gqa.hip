@@ -389,13 +389,39 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int n_items,
 constexpr int MF_D = 128;
 constexpr int MF_BM = 128;   // query rows per block (4 waves x 32)
 constexpr int MF_BN = 64;    // keys per tile
-constexpr int MF_KS = MF_D + 8;    // K tile row stride (bf16 elements)
-constexpr int MF_VS = MF_BN + 4;   // V^T tile row stride (bf16 elements)
+constexpr int MF_TILE = MF_BN * MF_D * 2;   // bytes of one K (or V) tile: 64 rows x 256 B
 
+// Byte offset of 16-byte chunk c of row r in a 64 x 256-byte tile. Chunks are XOR-swizzled
+// within 128-byte halves so rows read at the same column hit different LDS banks.
+__device__ __forceinline__ int mf_swz(int r, int c) { return r * 256 + ((c ^ (r & 7)) << 4); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4 *>(
+          reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void *>(
+                                          reinterpret_cast<uintptr_t>(lds_base)),
+                                   16, 0, 0);
+}
+
+// 128 query rows (4 waves x 32) against 64-key tiles, bf16 MFMA 32x32x16.
+//   S^T = K Q^T : A = K rows from LDS, B = Q in registers; a lane holds one query row
+//                 (column) and 16 keys, so the row softmax is lane-local plus one
+//                 exchange with lane ^ 32.
+//   O^T += V^T P^T : A = V^T read from the row-major V tile with the LDS transpose read
+//                 (ds_read_b64_tr_b16), B = P straight from the S^T registers (the key
+//                 order inside each 16-key step is permuted identically on both sides).
+// K/V tiles go global -> LDS with direct 16-byte loads, two stages: tile t+1 is in flight
+// while tile t is multiplied. Query rows are a request's new tokens x heads (extend,
+// causal) or the members of a shared radix segment x heads (decode partials).
 template <int G, bool SEG>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[MF_BN * MF_KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[MF_D * MF_VS];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
 
   const int tile = blockIdx.x, item = blockIdx.y, kvh = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -446,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + (q_tok * a.Hq + head) * MF_D + 8 * h;
 #pragma unroll
     for (int s = 0; s < MF_D / 16; ++s) {
-      u32x4 w = rvalid ? ldg16(qp + 16 * s) : u32x4{0, 0, 0, 0};
+      const u32x4 w = rvalid ? ldg16(qp + 16 * s) : u32x4{0, 0, 0, 0};
       qb[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -456,31 +482,45 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
 
+  // loaders: wave w fills rows 16w .. 16w+15 of each tile, 4 rows per instruction;
+  // lane i lands at byte 16*i of the instruction's 1 KB, i.e. row +i/16, physical chunk
+  // i%16, so it fetches logical chunk (i%16) ^ (row & 7) of that row.
   const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * MF_D * 2;
   const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * MF_D * 2;
   const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * MF_D * 2;
-  const int lr = tid >> 4, lc = tid & 15;   // loader: row within 16, 16-byte chunk
-
-  for (int kt = lo; kt < hi; kt += MF_BN) {
-    __syncthreads();
+  const int last = hi - 1;
+  int32_t sl[4];
+  auto load_slots = [&](int kt) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = lr + 16 * u;
-      const int key = kt + r;
-      u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
-      if (key < hi) {
-        const int64_t slot = rtt_row[key];
-        kv = ldg16(kb + slot * row_bytes + lc * 16);
-        vv = ldg16(vb + slot * row_bytes + lc * 16);
-      }
-      *reinterpret_cast<u32x4 *>(&Ks[r * MF_KS + lc * 8]) = kv;
+    for (int j = 0; j < 4; ++j) sl[j] = rtt_row[min(kt + wave * 16 + 4 * j + (lane >> 4), last)];
+  };
+  auto issue = [&](int stage) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(lc * 8 + 2 * e) * MF_VS + r] = static_cast<uint16_t>(vv[e] & 0xffffu);
-        Vt[(lc * 8 + 2 * e + 1) * MF_VS + r] = static_cast<uint16_t>(vv[e] >> 16);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 16 + 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 7);
+      const int64_t off = static_cast<int64_t>(sl[j]) * row_bytes + c * 16;
+      lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
+      lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
     }
-    __syncthreads();
+  };
+
+  if (lo < hi) {
+    load_slots(lo);
+    issue(0);
+    if (lo + MF_BN < hi) load_slots(lo + MF_BN);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int kt = lo, t = 0; kt < hi; kt += MF_BN, ++t) {
+    const int stage = t & 1;
+    if (kt + MF_BN < hi) {
+      issue(stage ^ 1);
+      if (kt + 2 * MF_BN < hi) load_slots(kt + 2 * MF_BN);
+    }
+    const uint8_t *Kt = smem[stage][0];
+    const uint8_t *Vt = smem[stage][1];
 
     f32x16 st[2];
 #pragma unroll
@@ -488,7 +528,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       st[mb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < MF_D / 16; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Ks[(mb * 32 + n) * MF_KS + 16 * s + 8 * h]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(mb * 32 + n, 2 * s + h));
         st[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], st[mb], 0, 0, 0);
       }
     }
@@ -532,20 +572,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
           w[e] = pack_bf16x2(st[mb][8 * j + 2 * e], st[mb][8 * j + 2 * e + 1]);
         pb[mb][j] = __builtin_bit_cast(bf16x8, w);
       }
+    // V^T operand: in each 16-lane group g, source lane s reads 4 dims of key row
+    // base + 4*(g>>1) + (s>>2) (+8 for the second read); the transpose hands lane s the
+    // 4 keys of value dim 16*(g&1) + s of the 32-dim block.
+    const int g = lane >> 4, s16 = lane & 15;
+    const int vrow0 = 4 * (g >> 1) + (s16 >> 2);
 #pragma unroll
     for (int dvb = 0; dvb < 4; ++dvb) {
-      const uint16_t *vrow = &Vt[(dvb * 32 + n) * MF_VS + 4 * h];
+      const int dv0 = dvb * 32 + 16 * (g & 1) + 4 * (s16 & 3);
+      const int c = dv0 >> 3, half = (dv0 >> 2) & 1;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const u32x2 lo2 = *reinterpret_cast<const u32x2 *>(vrow + mb * 32 + 16 * j);
-          const u32x2 hi2 = *reinterpret_cast<const u32x2 *>(vrow + mb * 32 + 16 * j + 8);
+          const int r0 = mb * 32 + 16 * j + vrow0;
+          const u32x2 lo2 = lds_tr16(Vt + mf_swz(r0, c) + 8 * half);
+          const u32x2 hi2 = lds_tr16(Vt + mf_swz(r0 + 8, c) + 8 * half);
           const u32x4 w = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
           o[dvb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[mb][j],
                                                            o[dvb], 0, 0, 0);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   if (!rvalid) return;
