@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
 
 
@@ -187,39 +189,49 @@ class Episode:
 
 
 def algorithmic(w, ep, name):
-    """Algorithmic work of one episode for a kernel family: (bytes, flops)."""
+    """Algorithmic work of one episode for a kernel family: (bytes, flops).
+
+    Bytes count each distinct KV row a launch must read once (plus its slot index),
+    queries read and final outputs written; partial results and re-reads are not
+    algorithmic. Flops: 2*Hq*(Dqk+Dv) per (query, key) pair."""
     s = w.shape
     eb_kv = {"f32": 4, "bf16": 2, "fp8": 1}[s.kv_dtype]
     eb_q = {"f32": 4, "bf16": 2}[s.q_dtype]
     row_kv = s.num_kv_heads * (s.head_dim_qk + (0 if s.v_is_k_prefix else s.head_dim_v)) * eb_kv \
-        + (4 if s.kv_dtype == "fp8" else 0)
+        + (4 if s.kv_dtype == "fp8" else 0) + 4
     q_row = s.num_q_heads * s.head_dim_qk * eb_q
     o_row = s.num_q_heads * s.head_dim_v * eb_q
+    pair_flops = 2.0 * s.num_q_heads * (s.head_dim_qk + s.head_dim_v)
     byt, flop = 0.0, 0.0
     for st, rnd in zip(ep.staged, ep.rounds):
         ph, B = st["ph"], st["B"]
         if name == "extend_mfma" and ph.extend == "attend":
             for a in rnd.admissions:
                 P, E = a.prefix_len, a.prompt_len - a.prefix_len
-                pairs = E * P + E * (E + 1) / 2
-                flop += 2.0 * s.num_q_heads * (s.head_dim_qk + s.head_dim_v) * pairs
+                flop += pair_flops * (E * P + E * (E + 1) / 2)
                 byt += (P + E) * row_kv + E * (q_row + o_row)
+        if name == "kv_store" and ph.extend != "host":
+            byt += 2 * st["T"] * row_kv
         if not ph.n_decode:
             continue
         plan = rnd.plan if ep.use_plan and B > 1 else None
+        seg_rows = float((plan.seg_end - plan.seg_start).sum()) if plan is not None else 0.0
         ps = plan.req_private_start if plan is not None else np.zeros(B, np.int32)
         for step in range(ph.n_decode):
             L = st["prompt_len"] + step + 1
-            if name in ("decode_tail_valu", "mla_decode"):
-                keys = (L - ps).sum()
-                byt += keys * (row_kv + 4) + B * q_row
-                flop += 2.0 * s.num_q_heads * (s.head_dim_qk + s.head_dim_v) * float(L.sum())
-            if name == "segment_mfma" and plan is not None:
-                seg_keys = (plan.seg_end - plan.seg_start).sum()
-                entries = len(plan.seg_members)
-                byt += seg_keys * (row_kv + 4) + entries * q_row
-            if name == "kv_store":
-                byt += 2 * B * row_kv
+            flop_step = pair_flops * float(L.sum())
+            if name == "mla_decode":
+                # distinct rows: shared prefixes once, the rest per request
+                shared = seg_rows
+                byt += (shared + float((L - ps).sum())) * row_kv + B * (q_row + o_row)
+                flop += flop_step
+            if name in ("decode_tail_valu", "decode_fused"):
+                byt += float((L - ps).sum()) * row_kv + B * (q_row + o_row)
+                flop += pair_flops * float((L - ps).sum())
+            if name in ("segment_mfma", "decode_fused") and plan is not None:
+                byt += seg_rows * row_kv
+                mem = np.diff(plan.seg_member_off)
+                flop += pair_flops * float(((plan.seg_end - plan.seg_start) * mem).sum())
     return byt, flop
 
 
@@ -266,6 +278,15 @@ def main():
     from prefix_shared_kv_radix_amd import _lib
     _lib.load()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}))
+        return
     w = workload_of(args.config)
     ep = Episode(w, not args.no_plan, args.splits)
     torch.cuda.synchronize()
@@ -316,7 +337,7 @@ def main():
     roof["traffic"] = None
     # decode-phase aggregate HBM rate over all decode kernels' algorithmic bytes
     dec_bytes = sum(algorithmic(w, ep, n)[0] for n in ("decode_tail_valu", "segment_mfma",
-                                                         "kv_store", "mla_decode") if n in kern)
+                                                         "decode_fused", "mla_decode") if n in kern)
     ext_flops = algorithmic(w, ep, "extend_mfma")[1]
     out = {
         "metric": "decode tokens/s + achieved HBM GB/s (% peak), prefix-shared KV attention",

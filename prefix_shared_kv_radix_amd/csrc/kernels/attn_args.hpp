@@ -77,5 +77,8 @@ hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, u
                 hipStream_t s);
 hipError_t mfma(int G, bool seg, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s);
 hipError_t combine(bool bf16, const AttnArgs &a, int batch, int Dv, hipStream_t s);
+// one launch: shared-segment MFMA tiles + private-tail waves, all writing partials
+hipError_t decode_fused(int G, const AttnArgs &a, int max_rows, unsigned seg_items,
+                        unsigned n_items, unsigned nsplit, hipStream_t s);
 
 }  // namespace radix_launch

@@ -109,11 +109,12 @@ enum KernelId {
   K_COMBINE = 6,
   K_MLA_DECODE = 7,
   K_MLA_COMBINE = 8,
-  K_COUNT = 9
+  K_DECODE_FUSED = 9,
+  K_COUNT = 10
 };
 const char *const kKernelNames[K_COUNT] = {
     "kv_store", "decode_tail_valu", "extend_valu", "segment_valu", "extend_mfma",
-    "segment_mfma", "combine", "mla_decode", "mla_combine"};
+    "segment_mfma", "combine", "mla_decode", "mla_combine", "decode_fused"};
 
 struct Profiler {
   std::vector<hipEvent_t> ev;
@@ -147,7 +148,7 @@ int seg_splits_for(const radix_attn_shape *s, const radix_decode_plan *plan) {
   const long rows = static_cast<long>(plan->max_members) * (mla ? 1 : G);
   const long tiles = mla ? rows : (rows + 127) / 128;
   const long blocks = tiles * plan->num_segments * s->num_kv_heads;
-  const long target = mla ? 1024 : 512;
+  const long target = mla ? 1024 : 256;   // the segment tiles overlap the tail waves
   long ss = (target + blocks - 1) / (blocks > 0 ? blocks : 1);
   const long cap = plan->max_seg_len / 256 > 1 ? plan->max_seg_len / 256 : 1;
   if (ss > cap) ss = cap;
@@ -418,10 +419,19 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     a.req_num_shared = plan->req_num_shared;
     a.private_start = plan->req_private_start;
     if (bf16) {
-      Timed t(K_SEGMENT_MFMA, s);
-      st = hip_status(radix_launch::mfma(G, true, a, plan->max_members * G,
-                                         static_cast<unsigned>(plan->num_segments * seg_splits), s),
-                      "segment launch");
+      // one launch: segment tiles and private-tail waves, then the merge
+      {
+        Timed t(K_DECODE_FUSED, s);
+        st = hip_status(radix_launch::decode_fused(
+                            G, a, plan->max_members * G,
+                            static_cast<unsigned>(plan->num_segments * seg_splits),
+                            static_cast<unsigned>(batch), static_cast<unsigned>(splits), s),
+                        "decode launch");
+      }
+      if (st != RADIX_OK) return st;
+      Timed t(K_COMBINE, s);
+      return hip_status(radix_launch::combine(bf16, a, batch, shape->head_dim_v, s),
+                        "combine launch");
     } else {
       Timed t(K_SEGMENT_VALU, s);
       st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, seg_splits, s),

@@ -140,12 +140,11 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
 // In MODE 0 and 3 the newest key (position seq_len-1) is read from k_new/v_new when given,
 // and the split-0 wave stores it into the pool and appends its slot to the slot list.
 template <typename T, int D, int G, int MODE>
-__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int n_items, int nsplit) {
+__device__ __forceinline__ void valu_body(const AttnArgs &a, int w, int n_items, int nsplit) {
   constexpr int EPL = Vec16<T>::N;
   static_assert(D / EPL == 16, "16 lanes per row");
   constexpr bool TAIL = MODE == 0 || MODE == 3;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
-  const int w = blockIdx.x * 4 + wave;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, sub = lane & 15;
   if (w >= n_items * nsplit * a.Hkv) return;
   const int kvh = w % a.Hkv;
   const int split = (w / a.Hkv) % nsplit;
@@ -385,6 +384,284 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int n_items,
   }
 }
 
+template <typename T, int D, int G, int MODE>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int n_items, int nsplit) {
+  valu_body<T, D, G, MODE>(a, blockIdx.x * 4 + (threadIdx.x >> 6), n_items, nsplit);
+}
+
+// ------------------------------------------------------------------ bf16 decode tail
+// One wave = one decode query (the G query heads of one KV head) over one key chunk,
+// for bf16 K/V with 128 dims. Eight lanes cover a 256-byte row (32 bytes each), so an
+// iteration of 16 rows gives every lane two rows (r and r+8 of the iteration).
+//   q.k  : v_dot2_f32_bf16 on packed pairs, then a 3-step DPP sum over the 8 lanes
+//   p.v  : p of the two rows packed to bf16, V dims of the two rows paired with byte
+//          permutes, v_dot2_f32_bf16 per dim (fp32 accumulation)
+// The running maximum is refreshed only when some head's tile maximum exceeds it by
+// more than 2^8 (numerator and denominator share the stale maximum, so nothing is lost).
+// MODE 0 writes a partial; MODE 3 writes the output, merged with the request's
+// shared-segment partials. The newest key is read from k_new/v_new when given and the
+// chunk-0 wave stores it and appends its slot.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// sum over each group of 8 consecutive lanes (quad_perm [1,0,3,2], [2,3,0,1], half mirror)
+__device__ __forceinline__ float sum8(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+  return x;
+}
+
+#ifndef RADIX_TAIL_STAGES
+#define RADIX_TAIL_STAGES 3
+#endif
+
+template <int G, int MODE>
+__device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_items, int nsplit) {
+  constexpr int D = 128;
+  constexpr int NB = RADIX_TAIL_STAGES;
+  constexpr float kGrow = 8.f;
+  const int lane = threadIdx.x & 63, r8 = lane >> 3, sub = lane & 7;
+  if (w >= n_items * nsplit * a.Hkv) return;
+  const int kvh = w % a.Hkv;
+  const int split = (w / a.Hkv) % nsplit;
+  const int b = w / (a.Hkv * nsplit);
+
+  const int hi = a.seq_lens[b];
+  const int lo = a.private_start ? a.private_start[b] : 0;
+  const int64_t q_row = b;
+  const int32_t *rtt_row = rtt_row_of(a, b);
+  const int part = a.part_base + split;
+  const int chunk = nsplit > 1 ? a.split_chunk : ((hi - lo + 15) & ~15);
+  const int s_lo = lo + split * chunk;
+  const int s_hi = min(hi, s_lo + chunk);
+
+  const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * D * 2;
+  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * D * 2 + sub * 32;
+  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * 2 + sub * 32;
+  const bool fuse_new = a.k_new != nullptr;
+  const char *knew = nullptr, *vnew = nullptr;
+  if (fuse_new) {
+    const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D * 2 + sub * 32;
+    knew = reinterpret_cast<const char *>(a.k_new) + off;
+    vnew = reinterpret_cast<const char *>(a.v_new) + off;
+    if (split == 0 && r8 == 0) {
+      const int64_t at = static_cast<int64_t>(a.req_rows ? a.req_rows[b] : b) * a.rtt_stride + hi - 1;
+      const int64_t slot = a.new_slots ? a.new_slots[b] : a.rtt[at];
+      if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[at] = static_cast<int32_t>(slot);
+      char *kd = const_cast<char *>(kb) + slot * row_bytes;
+      char *vd = const_cast<char *>(vb) + slot * row_bytes;
+      *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
+      *reinterpret_cast<u32x4 *>(kd + 16) = ldg16(knew + 16);
+      *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
+      *reinterpret_cast<u32x4 *>(vd + 16) = ldg16(vnew + 16);
+    }
+  }
+
+  // q: G heads x this lane's 16 dims, packed bf16 pairs (unscaled)
+  uint32_t qp[G][8];
+  {
+    const char *qb = reinterpret_cast<const char *>(a.q) + (q_row * a.Hq + kvh * G) * D * 2 + sub * 32;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const u32x4 x0 = ldg16(qb + h * D * 2), x1 = ldg16(qb + h * D * 2 + 16);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        qp[h][c] = x0[c];
+        qp[h][4 + c] = x1[c];
+      }
+    }
+  }
+  float m[G], l[G], acc[G][16];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegBig;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
+  }
+
+  // iteration t covers rows base .. base+15; this lane takes rows base + r8 and base + 8 + r8.
+  // Rows past the chunk point at a finite stored row (the newest key when fused, else the
+  // chunk's last row), so no masking of V is needed: their weight is exactly 0.
+  const int last = s_hi - 1;
+  u32x4 kbuf[NB][2][2], vbuf[NB][2][2];
+  int32_t sbuf[NB][2];
+  auto load_slots = [&](int base, int32_t *sl) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int r = base + 8 * g + r8;
+      const int32_t v = rtt_row[min(r, last)];
+      sl[g] = v;
+    }
+  };
+  auto load_kv = [&](int base, const int32_t *sl, u32x4 (*kd)[2], u32x4 (*vd)[2]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int r = base + 8 * g + r8;
+      const bool use_new = fuse_new && (r >= hi - 1 || r >= s_hi);
+      const char *kp = use_new ? knew : kb + static_cast<int64_t>(sl[g]) * row_bytes;
+      const char *vp = use_new ? vnew : vb + static_cast<int64_t>(sl[g]) * row_bytes;
+      kd[g][0] = ldg16(kp);
+      kd[g][1] = ldg16(kp + 16);
+      vd[g][0] = ldg16(vp);
+      vd[g][1] = ldg16(vp + 16);
+    }
+  };
+  auto compute = [&](int base, const u32x4 (*kr)[2], const u32x4 (*vr)[2]) {
+    float s[2][G];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bool valid = base + 8 * g + r8 < s_hi;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          d = dot2bf(qp[h][c], kr[g][0][c], d);
+          d = dot2bf(qp[h][4 + c], kr[g][1][c], d);
+        }
+        d = sum8(d);
+        s[g][h] = valid ? d * a.scale_log2 : -INFINITY;
+      }
+    }
+    bool grow = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) grow |= fmaxf(s[0][h], s[1][h]) > m[h] + kGrow;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], fmaxf(s[0][h], s[1][h]));
+        const float alpha = exp2f(m[h] - mn);
+        m[h] = mn;
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
+      }
+    }
+    uint32_t pp[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p0 = exp2f(s[0][h] - m[h]), p1 = exp2f(s[1][h] - m[h]);
+      l[h] += p0 + p1;
+      pp[h] = pack2bf(p0, p1);
+    }
+    // pair dim e of row g=0 with dim e of row g=1
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t a0 = vr[0][c >> 2][c & 3], a1 = vr[1][c >> 2][c & 3];
+      const uint32_t lo2 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // {row0.lo, row1.lo}
+      const uint32_t hi2 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // {row0.hi, row1.hi}
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h][2 * c] = dot2bf(pp[h], lo2, acc[h][2 * c]);
+        acc[h][2 * c + 1] = dot2bf(pp[h], hi2, acc[h][2 * c + 1]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < NB; ++j) load_slots(s_lo + 16 * j, sbuf[j]);
+#pragma unroll
+  for (int j = 0; j + 1 < NB; ++j) load_kv(s_lo + 16 * j, sbuf[j], kbuf[j], vbuf[j]);
+  for (int base = s_lo; base < s_hi; base += 16 * NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int it = base + 16 * j;
+      if (it >= s_hi) break;
+      const int jl = (j + NB - 1) % NB;
+      const int ahead = it + 16 * (NB - 1);
+      load_slots(ahead + 16, sbuf[j]);
+      load_kv(ahead, sbuf[jl], kbuf[jl], vbuf[jl]);
+      compute(it, kbuf[j], vbuf[j]);
+    }
+  }
+
+  // merge the 8 row groups (lanes l, l^8, l^16, l^32 hold the same dims)
+#pragma unroll
+  for (int mask = 8; mask <= 32; mask <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = shfl_xor_f(m[h], mask), lo_ = shfl_xor_f(l[h], mask);
+      const float mn = fmaxf(m[h], mo);
+      const float wa = exp2f(m[h] - mn), wb = exp2f(mo - mn);
+      l[h] = l[h] * wa + lo_ * wb;
+      m[h] = mn;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[h][e] = acc[h][e] * wa + shfl_xor_f(acc[h][e], mask) * wb;
+    }
+  }
+
+  // group r8 writes (head, half) pairs r8, r8 + 8, ...: 8 dims each
+  const int nshared = (MODE == 3 && a.req_num_shared) ? a.req_num_shared[b] * a.seg_splits : 0;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (((2 * h + half) & 7) != r8) continue;
+      const int head = kvh * G + h;
+      const int d0 = sub * 16 + half * 8;
+      float M = m[h], L = l[h];
+      float O[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[e] = acc[h][half * 8 + e];
+      if (MODE == 3) {
+        const int64_t hp = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
+        for (int p0 = 0; p0 < nshared; p0 += 4) {
+          float pl[4];
+          f32x4 po[4][2];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = p0 + j < nshared;
+            pl[j] = ok ? a.ws_lse[hp + p0 + j] : -INFINITY;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              po[j][c] = ok ? *reinterpret_cast<const f32x4 *>(a.ws_o + (hp + p0 + j) * D + d0 + 4 * c)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float mn = fmaxf(M, pl[j]);
+            const float wa = exp2f(M - mn), wb = exp2f(pl[j] - mn);
+            L = L * wa + wb;
+            M = mn;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) O[4 * c + e] = O[4 * c + e] * wa + po[j][c][e] * wb;
+          }
+        }
+      }
+      const bool empty = !(L > 0.f);
+      const float inv = empty ? 0.f : 1.f / L;
+      const float lse2 = empty ? -INFINITY : M + log2f(L);
+      if (MODE == 3) {
+        uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + (q_row * a.Hq + head) * D + d0;
+        *reinterpret_cast<u32x4 *>(op) = u32x4{pack2bf(O[0] * inv, O[1] * inv), pack2bf(O[2] * inv, O[3] * inv),
+                                               pack2bf(O[4] * inv, O[5] * inv), pack2bf(O[6] * inv, O[7] * inv)};
+        if (a.lse && d0 == 0) a.lse[q_row * a.Hq + head] = lse2 * kLn2;
+      } else {
+        const int64_t pi = (static_cast<int64_t>(b) * a.Hq + head) * a.parts + part;
+        float *wp = a.ws_o + pi * D + d0;
+        *reinterpret_cast<f32x4 *>(wp) = f32x4{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
+        *reinterpret_cast<f32x4 *>(wp + 4) = f32x4{O[4] * inv, O[5] * inv, O[6] * inv, O[7] * inv};
+        if (d0 == 0) a.ws_lse[pi] = lse2;
+      }
+    }
+}
+
+template <int G, int MODE>
+__global__ __launch_bounds__(256) void tail_bf16_kernel(AttnArgs a, int n_items, int nsplit) {
+  tail_bf16_body<G, MODE>(a, blockIdx.x * 4 + (threadIdx.x >> 6), n_items, nsplit);
+}
+
 // ------------------------------------------------------------------ MFMA kernel
 constexpr int MF_D = 128;
 constexpr int MF_BM = 128;   // query rows per block (4 waves x 32)
@@ -420,10 +697,8 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
 // while tile t is multiplied. Query rows are a request's new tokens x heads (extend,
 // causal) or the members of a shared radix segment x heads (decode partials).
 template <int G, bool SEG>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
-
-  const int tile = blockIdx.x, item = blockIdx.y, kvh = blockIdx.z;
+__device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item, int kvh,
+                                          uint8_t (*smem)[2][MF_TILE]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
 
@@ -630,6 +905,41 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
+// Blocks of one launch in 1-D order: consecutive logical blocks (the tiles that read the
+// same K/V rows) are placed on the same XCD, since block b runs on XCD b % 8.
+__device__ __forceinline__ int xcd_logical(int bid, int nblocks) {
+  const int per = (nblocks + 7) / 8;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// logical block -> (tile, item, kvh), tile fastest
+template <int G, bool SEG>
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
+  const int nblocks = tiles * items * a.Hkv;
+  const int lb = xcd_logical(blockIdx.x, nblocks);
+  if (lb >= nblocks) return;
+  mfma_body<G, SEG>(a, lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
+}
+
+// One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
+// the rest are private-tail waves (4 per block); both write partials that
+// combine_kernel merges. Matrix-core work and the memory-bound tail overlap.
+template <int G>
+__global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int tiles, int seg_items,
+                                                             int n_items, int nsplit) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];
+  const int seg_blocks = 8 * ((tiles * seg_items * a.Hkv + 7) / 8);
+  if (static_cast<int>(blockIdx.x) < seg_blocks) {
+    const int nblocks = tiles * seg_items * a.Hkv;
+    const int lb = xcd_logical(blockIdx.x, nblocks);
+    if (lb >= nblocks) return;
+    mfma_body<G, true>(a, lb % tiles, (lb / tiles) % seg_items, lb / (tiles * seg_items), smem);
+  } else {
+    tail_bf16_body<G, 0>(a, (blockIdx.x - seg_blocks) * 4 + (threadIdx.x >> 6), n_items, nsplit);
+  }
+}
+
 // ------------------------------------------------------------------ combine
 template <typename T>
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a, int Dv) {
@@ -694,9 +1004,30 @@ static hipError_t valu_g(int G, int mode, const AttnArgs &a, unsigned items, uns
   return hipErrorInvalidValue;
 }
 
+template <int G>
+static hipError_t launch_tail(int mode, const AttnArgs &a, unsigned items, unsigned splits,
+                              hipStream_t stream) {
+  const uint64_t waves = static_cast<uint64_t>(items) * splits * a.Hkv;
+  if (waves > 0x7fffffffull) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+  const int n = static_cast<int>(items), ns = static_cast<int>(splits);
+  if (mode == 0) tail_bf16_kernel<G, 0><<<grid, block, 0, stream>>>(a, n, ns);
+  else tail_bf16_kernel<G, 3><<<grid, block, 0, stream>>>(a, n, ns);
+  return hipGetLastError();
+}
+
 hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, unsigned splits,
                 hipStream_t s) {
   if (items == 0) return hipSuccess;
+  if (bf16 && (mode == 0 || mode == 3)) {
+    switch (G) {
+      case 1: return launch_tail<1>(mode, a, items, splits, s);
+      case 2: return launch_tail<2>(mode, a, items, splits, s);
+      case 4: return launch_tail<4>(mode, a, items, splits, s);
+      case 8: return launch_tail<8>(mode, a, items, splits, s);
+    }
+    return hipErrorInvalidValue;
+  }
   return bf16 ? valu_g<uint16_t, 128>(G, mode, a, items, splits, s)
               : valu_g<float, 64>(G, mode, a, items, splits, s);
 }
@@ -704,10 +1035,35 @@ hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, u
 template <int G>
 static hipError_t launch_mfma(bool seg, const AttnArgs &a, unsigned tiles, unsigned items,
                               hipStream_t s) {
-  dim3 grid(tiles, items, a.Hkv), block(256);
-  if (seg) attn_mfma_kernel<G, true><<<grid, block, 0, s>>>(a);
-  else attn_mfma_kernel<G, false><<<grid, block, 0, s>>>(a);
+  const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
+  if (n > 0x7fffffffull) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(256);
+  if (seg) attn_mfma_kernel<G, true><<<grid, block, 0, s>>>(a, tiles, items);
+  else attn_mfma_kernel<G, false><<<grid, block, 0, s>>>(a, tiles, items);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_fused(const AttnArgs &a, unsigned tiles, unsigned seg_items,
+                               unsigned n_items, unsigned nsplit, hipStream_t s) {
+  const uint64_t seg_blocks = 8 * ((static_cast<uint64_t>(tiles) * seg_items * a.Hkv + 7) / 8);
+  const uint64_t tail_blocks = (static_cast<uint64_t>(n_items) * nsplit * a.Hkv + 3) / 4;
+  if (seg_blocks + tail_blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  decode_fused_kernel<G><<<dim3(static_cast<unsigned>(seg_blocks + tail_blocks)), dim3(256), 0, s>>>(
+      a, tiles, seg_items, n_items, nsplit);
+  return hipGetLastError();
+}
+
+hipError_t decode_fused(int G, const AttnArgs &a, int max_rows, unsigned seg_items,
+                        unsigned n_items, unsigned nsplit, hipStream_t s) {
+  const unsigned tiles = static_cast<unsigned>((max_rows + MF_BM - 1) / MF_BM);
+  switch (G) {
+    case 1: return launch_fused<1>(a, tiles, seg_items, n_items, nsplit, s);
+    case 2: return launch_fused<2>(a, tiles, seg_items, n_items, nsplit, s);
+    case 4: return launch_fused<4>(a, tiles, seg_items, n_items, nsplit, s);
+    case 8: return launch_fused<8>(a, tiles, seg_items, n_items, nsplit, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t mfma(int G, bool seg, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
