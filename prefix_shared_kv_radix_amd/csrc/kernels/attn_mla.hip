@@ -7,12 +7,17 @@
 // KV rows are bf16, or OCP E4M3 bytes with one fp32 scale per token (KV cache FP8,
 // same section), dequantised to bf16 as they are staged into LDS.
 //
-// Block = one request's 128 heads over one key range; 4 waves x 32 heads. Per
-// 32-key tile: S^T = K Q^T (MFMA 32x32x16, query head per lane column), online
-// softmax in registers, O^T += V^T P^T (MFMA, 16 blocks of 32 value dims). Tiles
-// are double-buffered in LDS: the next tile's rows are loaded into registers
-// while the current one is multiplied. With one chunk per request the block
-// writes the output; with several, partials (o, lse) that combine_kernel merges.
+// Block = one request's 128 heads over one key range, 8 waves. Waves w and w+4 share
+// the 32 heads 32*(w%4) .. +31 and split the work by dimension: wave half 0 takes QK
+// dims 0..287 and value dims 0..255, half 1 the rest. Per 32-key tile each wave forms
+// a partial S^T = K Q^T over its dims (MFMA 32x32x16, query head per lane column),
+// the pair swaps partials through LDS and both add them in the same order, so both
+// run the identical online softmax; then O^T += V^T P^T over the wave's value dims.
+// Per wave that is 72 registers of Q and 128 accumulator registers of O, which fits
+// two waves per SIMD. Tiles are double-buffered in LDS (bf16 rows go straight from
+// global memory to LDS; fp8 rows pass through registers to be dequantised). With one
+// chunk per request the block writes the output; with several, partials (o, lse)
+// that combine_kernel merges.
 #include "attn_args.hpp"
 #include "common.hpp"
 
@@ -23,115 +28,114 @@ namespace {
 
 constexpr int kDqk = 576, kDv = 512, kHeads = 128;
 constexpr int kBN = 32;              // keys per tile
-constexpr int kKS = kDqk + 8;        // K tile row stride (bf16 elements)
-constexpr int kVS = kBN + 4;         // V^T tile row stride (bf16 elements)
-constexpr float kRescaleLog2 = 8.f;  // tolerated growth of the running max before rescaling
+constexpr int kHalfQK = kDqk / 2;    // QK dims per wave
+constexpr int kHalfV = kDv / 2;      // value dims per wave
+constexpr float kRescaleLog2 = 8.f;
+#ifndef RADIX_MLA_FENCE
+#define RADIX_MLA_FENCE 3   // score MFMAs between scheduling fences (bounds live K operands)
+#endif  // tolerated growth of the running max before rescaling
 
 __device__ __forceinline__ float xor32f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ 32) << 2,
                                                                  __builtin_bit_cast(int, x)));
 }
 
-// Staging of one tile: thread t loads key (t >> 3), chunk group (t & 7) = 144 bytes of
-// a bf16 row (9 x 16 B) or 72 bytes of an fp8 row (9 x 8 B).
-template <bool FP8> struct Stage;
-template <> struct Stage<false> {
-  u32x4 w[9];
-  float scale;
-  __device__ void load(const uint8_t *row) {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) w[i] = *reinterpret_cast<const u32x4 *>(row + 16 * i);
-  }
-  __device__ void zero() {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) w[i] = u32x4{0, 0, 0, 0};
-  }
-  __device__ u32x4 bf16x8(int i) const { return w[i]; }
-};
-template <> struct Stage<true> {
-  u32x2 w[9];
-  float scale;
-  __device__ void load(const uint8_t *row) {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) w[i] = *reinterpret_cast<const u32x2 *>(row + 8 * i);
-  }
-  __device__ void zero() {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) w[i] = u32x2{0, 0};
-    scale = 0.f;
-  }
-  __device__ u32x4 bf16x8(int i) const {
-    const uint32_t a = w[i][0], b = w[i][1];
-    return u32x4{pack_bf16x2(fp8_to_f32<0>(a) * scale, fp8_to_f32<1>(a) * scale),
-                 pack_bf16x2(fp8_to_f32<2>(a) * scale, fp8_to_f32<3>(a) * scale),
-                 pack_bf16x2(fp8_to_f32<0>(b) * scale, fp8_to_f32<1>(b) * scale),
-                 pack_bf16x2(fp8_to_f32<2>(b) * scale, fp8_to_f32<3>(b) * scale)};
-  }
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4 *>(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void *>(
+                                          reinterpret_cast<uintptr_t>(lds_base)),
+                                   16, 0, 0);
+}
 
-template <bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_decode_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kDv * kVS];
+// Tile layout in LDS (bf16, 36 KB per 32 keys): region A holds dims 0..511 of key r as
+// one 1 KB row, 16-byte chunk c at r*1024 + 16*(c ^ fA(r)); region B holds the rope
+// dims 512..575 as 128-byte rows after it, chunk 64+c at 32768 + r*128 + 16*(c ^ fB(r)).
+// fA mixes both 2-bit fields of the row so that the score reads (16 rows, one chunk)
+// and the transposed value reads (8 rows, 4 chunks) both fall on distinct banks; fB
+// does the same for the 128-byte rows. One 1 KB wave-wide direct load fills one
+// region-A row, so each load's slot is one scalar.
+constexpr int kTileB = kBN * 2 * kDqk;   // 36 KB
+constexpr int kRegB = kBN * 1024;        // start of region B
+__device__ __forceinline__ int fA(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int fB(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int offA(int r, int c) { return r * 1024 + ((c ^ fA(r)) << 4); }
+__device__ __forceinline__ int offB(int r, int c) { return kRegB + r * 128 + ((c ^ fB(r)) << 4); }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <bool FP8, int HALF>
+__device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTileB],
+                                         f32x4 (*xs)[4][64], int wave, int b, int lo, int hi,
+                                         int part) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int hg = wave & 3;
   const int n = lane & 31, h = lane >> 5;
-
-  // ---- work item: requests in plan order (members of one shared segment are
-  // consecutive) spread so that consecutive items land on one XCD; each request's
-  // keys [0, seq_len) are cut into nsplit chunks
-  const int items = a.batch * a.nsplit;
-  const int per_xcd = (items + 7) / 8;
-  const int pos = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (pos >= items) return;
-  const int split = pos % a.nsplit;
-  const int b = a.req_order ? a.req_order[pos / a.nsplit] : pos / a.nsplit;
-  const int L = a.seq_lens[b];
-  const int lo = split * a.split_chunk;
-  const int hi = min(L, lo + a.split_chunk);
-  const int part = split;
   const int32_t *rtt_row = a.rtt + static_cast<int64_t>(a.req_rows ? a.req_rows[b] : b) * a.rtt_stride;
 
-  // ---- Q (B operand of S^T = K Q^T): this lane's head, dims 16s + 8h .. +7
-  const int head = wave * 32 + n;
-  bf16x8 qb[kDqk / 16];
+  // ---- Q (B operand of S^T = K Q^T): this lane's head, dims HALF*288 + 16s + 8h .. +7
+  const int head = hg * 32 + n;
+  bf16x8 qb[kHalfQK / 16];
   {
-    const uint16_t *qp = a.q + (static_cast<int64_t>(b) * kHeads + head) * kDqk + 8 * h;
+    const uint16_t *qp = a.q + (static_cast<int64_t>(b) * kHeads + head) * kDqk + kHalfQK * HALF + 8 * h;
 #pragma unroll
-    for (int s = 0; s < kDqk / 16; ++s) qb[s] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * s));
+    for (int s = 0; s < kHalfQK / 16; ++s) qb[s] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * s));
   }
-  f32x16 o[kDv / 32];
+  f32x16 o[kHalfV / 32];
 #pragma unroll
-  for (int i = 0; i < kDv / 32; ++i) o[i] = f32x16{};
+  for (int i = 0; i < kHalfV / 32; ++i) o[i] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
 
-  // ---- staging
-  constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;
-  const int skey = tid >> 3, sgrp = tid & 7;
+  // ---- tile loads. bf16: region-A row J by wave J % 8 (lane i brings logical chunk
+  // i ^ fA(J)); region B by waves 0..3 (lane i: row 8*wave + i/8, chunk i%8 ^ fB(row)).
+  // Lane r holds the slot of row r (lanes 32..63 repeat). fp8: 16 threads per row,
+  // thread converts 8-byte groups fsub + 16i (< 72) of row tid/16 into bf16 chunks.
   const uint8_t *kv = static_cast<const uint8_t *>(a.kv);
-  Stage<FP8> st;
-  auto fetch = [&](int kt) {
-    const int key = kt + skey;
-    if (key < hi) {
-      const int64_t slot = rtt_row[key];
-      st.load(kv + slot * kRowBytes + sgrp * (FP8 ? 72 : 144));
-      if (FP8) st.scale = a.kv_scale[slot];
+  const int last = hi - 1;
+  const int frow = tid >> 4, fsub = tid & 15;
+  int32_t sl;
+  u32x2 raw[FP8 ? 5 : 1];
+  float rscale = 0.f;
+  auto load_slots = [&](int kt) { sl = rtt_row[min(kt + (FP8 ? frow : (lane & 31)), last)]; };
+  auto issue = [&](int kt, int stage) {
+    if (FP8) {
+      const uint8_t *src = kv + static_cast<int64_t>(sl) * kDqk;
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+        raw[i] = *reinterpret_cast<const u32x2 *>(src + 8 * min(fsub + 16 * i, 71));
+      rscale = (kt + frow < hi) ? a.kv_scale[sl] : 0.f;
     } else {
-      st.zero();
+#pragma unroll
+      for (int jj = 0; jj < kBN / 8; ++jj) {
+        const int J = wave + 8 * jj;
+        const int64_t slot = __builtin_amdgcn_readlane(sl, J);
+        lds_load16(kv + slot * (2 * kDqk) + ((lane ^ fA(J)) << 4), &smem[stage][J * 1024]);
+      }
+      if (wave < 4) {
+        const int r = 8 * wave + (lane >> 3);
+        const int64_t slot = __builtin_amdgcn_ds_bpermute(r << 2, sl);
+        lds_load16(kv + slot * (2 * kDqk) + 1024 + (((lane & 7) ^ fB(r)) << 4),
+                   &smem[stage][kRegB + wave * 1024]);
+      }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int stage) {   // fp8 only: dequantise the registers into the bf16 tile
+    if (FP8) {
+      int tv = tid;
+      asm volatile("" : "+v"(tv));
+      const int frow = tv >> 4, fsub = tv & 15;
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
-      const int c = sgrp * 9 + i;            // 16-byte chunk (8 dims) of the 576-dim row
-      const u32x4 w = st.bf16x8(i);
-      *reinterpret_cast<u32x4 *>(&Ks[buf][skey * kKS + c * 8]) = w;
-      if (c < kDv / 8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Vt[buf][(c * 8 + 2 * e) * kVS + skey] = static_cast<uint16_t>(w[e] & 0xffffu);
-          Vt[buf][(c * 8 + 2 * e + 1) * kVS + skey] = static_cast<uint16_t>(w[e] >> 16);
+      for (int i = 0; i < 5; ++i) {
+        const int c = fsub + 16 * i;
+        if (c < 72) {
+          const uint32_t x = raw[i][0], y = raw[i][1];
+          const u32x4 w = u32x4{pack_bf16x2(fp8_to_f32<0>(x) * rscale, fp8_to_f32<1>(x) * rscale),
+                                pack_bf16x2(fp8_to_f32<2>(x) * rscale, fp8_to_f32<3>(x) * rscale),
+                                pack_bf16x2(fp8_to_f32<0>(y) * rscale, fp8_to_f32<1>(y) * rscale),
+                                pack_bf16x2(fp8_to_f32<2>(y) * rscale, fp8_to_f32<3>(y) * rscale)};
+          *reinterpret_cast<u32x4 *>(&smem[stage][c < 64 ? offA(frow, c) : offB(frow, c - 64)]) = w;
         }
       }
     }
@@ -139,21 +143,54 @@ void mla_decode_kernel(MlaArgs a) {
 
   const int ntiles = hi > lo ? (hi - lo + kBN - 1) / kBN : 0;
   if (ntiles > 0) {
-    fetch(lo);
-    stash(0);
+    load_slots(lo);
+    issue(lo, 0);
+    if (FP8) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      stash(0);
+    }
+    if (ntiles > 1) load_slots(lo + kBN);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // V^T operand from the tile: in 16-lane group g, source lane s reads 4 value dims of
+  // key row 16j + 4*(g>>1) + (s>>2) (+8 for the second read)
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int kt = lo + t * kBN;
-    if (t + 1 < ntiles) fetch(kt + kBN);
+    if (t + 1 < ntiles) {
+      issue(kt + kBN, buf ^ 1);
+      if (t + 2 < ntiles) load_slots(kt + 2 * kBN);
+    }
+    const uint8_t *T = smem[buf];
+    // lane-derived LDS offsets are recomputed each tile (cheap VALU) rather than held
+    // in registers across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int n = ln & 31, h = ln >> 5, g = ln >> 4, s16 = ln & 15;
+    const int vrow = 4 * (g >> 1) + (s16 >> 2);
 
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < kDqk / 16; ++s) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Ks[buf][n * kKS + 16 * s + 8 * h]);
+    for (int s = 0; s < kHalfQK / 16; ++s) {
+      const int c = (kHalfQK / 8) * HALF + 2 * s + h;   // < 64 exactly when the pair is
+      const int off = (kHalfQK / 8) * HALF + 2 * s < 64 ? offA(n, c) : offB(n, c - 64);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(T + off);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sc, 0, 0, 0);
+      if (s % RADIX_MLA_FENCE == RADIX_MLA_FENCE - 1) __builtin_amdgcn_sched_barrier(0);
     }
+    // swap partial scores with the other half of the pair; both add own + other
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xs[wave][q][lane] = f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 other = xs[wave ^ 4][q][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[4 * q + e] += other[e];
+    }
+
     float mx = kNegBig;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -170,7 +207,7 @@ void mla_decode_kernel(MlaArgs a) {
       const float alpha = exp2f(m_run - mn);
       l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < kDv / 32; ++d) o[d] *= alpha;
+      for (int d = 0; d < kHalfV / 32; ++d) o[d] *= alpha;
       m_run = mn;
     }
     float rs = 0.f;
@@ -190,29 +227,36 @@ void mla_decode_kernel(MlaArgs a) {
       pb[j] = __builtin_bit_cast(bf16x8, w);
     }
 #pragma unroll
-    for (int d = 0; d < kDv / 32; ++d) {
-      const uint16_t *vrow = &Vt[buf][(d * 32 + n) * kVS + 4 * h];
+    for (int d = 0; d < kHalfV / 32; ++d) {
+      const int dv0 = kHalfV * HALF + d * 32 + 16 * (g & 1) + 4 * (s16 & 3);
+      const int c = dv0 >> 3, hb = (dv0 >> 2) & 1;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x2 lo2 = *reinterpret_cast<const u32x2 *>(vrow + 16 * j);
-        const u32x2 hi2 = *reinterpret_cast<const u32x2 *>(vrow + 16 * j + 8);
+        const int r0 = 16 * j + vrow;
+        const u32x2 lo2 = lds_tr16(T + offA(r0, c) + 8 * hb);
+        const u32x2 hi2 = lds_tr16(T + offA(r0 + 8, c) + 8 * hb);
         const u32x4 w = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[j], o[d],
                                                         0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) stash(buf ^ 1);
+    if (FP8 && t + 1 < ntiles) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      stash(buf ^ 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  // ---- partial (normalised o, lse in log2 units) or, for a single part, the output
+  // ---- partial (normalised o, lse in log2 units) or, for a single part, the output;
+  // each wave of the pair writes its value dims, half 0 the lse
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse2 = empty ? -INFINITY : m_run + log2f(l_run);
   if (a.parts == 1 && a.out) {
-    uint16_t *op = a.out + (static_cast<int64_t>(b) * kHeads + head) * kDv;
+    uint16_t *op = a.out + (static_cast<int64_t>(b) * kHeads + head) * kDv + kHalfV * HALF;
 #pragma unroll
-    for (int d = 0; d < kDv / 32; ++d)
+    for (int d = 0; d < kHalfV / 32; ++d)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int dv = d * 32 + 8 * g4 + 4 * h;
@@ -220,20 +264,43 @@ void mla_decode_kernel(MlaArgs a) {
             u32x2{pack_bf16x2(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv),
                   pack_bf16x2(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv)};
       }
-    if (a.lse && h == 0) a.lse[static_cast<int64_t>(b) * kHeads + head] = lse2 * kLn2;
+    if (a.lse && h == 0 && HALF == 0) a.lse[static_cast<int64_t>(b) * kHeads + head] = lse2 * kLn2;
     return;
   }
   const int64_t pi = (static_cast<int64_t>(b) * kHeads + head) * a.parts + part;
-  float *wp = a.ws_o + pi * kDv;
+  float *wp = a.ws_o + pi * kDv + kHalfV * HALF;
 #pragma unroll
-  for (int d = 0; d < kDv / 32; ++d)
+  for (int d = 0; d < kHalfV / 32; ++d)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int dv = d * 32 + 8 * g4 + 4 * h;
       *reinterpret_cast<f32x4 *>(wp + dv) = f32x4{o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv,
                                                   o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv};
     }
-  if (h == 0) a.ws_lse[pi] = lse2;
+  if (h == 0 && HALF == 0) a.ws_lse[pi] = lse2;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mla_decode_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][kTileB];
+  __shared__ __attribute__((aligned(16))) f32x4 xs[8][4][64];   // partial scores per wave
+
+  // ---- work item: requests in plan order (members of one shared segment are
+  // consecutive) spread so that consecutive items land on one XCD; each request's
+  // keys [0, seq_len) are cut into nsplit chunks
+  const int items = a.batch * a.nsplit;
+  const int per_xcd = (items + 7) / 8;
+  const int pos = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (pos >= items) return;
+  const int split = pos % a.nsplit;
+  const int b = a.req_order ? a.req_order[pos / a.nsplit] : pos / a.nsplit;
+  const int L = a.seq_lens[b];
+  const int lo = split * a.split_chunk;
+  const int hi = min(L, lo + a.split_chunk);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave < 4) mla_body<FP8, 0>(a, smem, xs, wave, b, lo, hi, split);
+  else mla_body<FP8, 1>(a, smem, xs, wave, b, lo, hi, split);
 }
 
 }  // namespace
@@ -247,8 +314,8 @@ unsigned mla_blocks(const MlaArgs &a) {
 hipError_t mla(const MlaArgs &a, hipStream_t s) {
   const unsigned blocks = mla_blocks(a);
   if (blocks == 0) return hipSuccess;
-  if (a.fp8) mla_decode_kernel<true><<<dim3(blocks), dim3(256), 0, s>>>(a);
-  else mla_decode_kernel<false><<<dim3(blocks), dim3(256), 0, s>>>(a);
+  if (a.fp8) mla_decode_kernel<true><<<dim3(blocks), dim3(512), 0, s>>>(a);
+  else mla_decode_kernel<false><<<dim3(blocks), dim3(512), 0, s>>>(a);
   return hipGetLastError();
 }
 
