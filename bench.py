@@ -235,6 +235,49 @@ def algorithmic(w, ep, name):
     return byt, flop
 
 
+KERNEL_DIR = os.path.join(ROOT, "prefix_shared_kv_radix_amd", "csrc", "kernels")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_digest():
+    """sha256 over the device kernel sources: counter figures taken from another
+    digest describe other code and are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(KERNEL_DIR)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            with open(os.path.join(KERNEL_DIR, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3
+    counter summaries: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the
+    kernel's dispatches), each scaled by what it reads for a plain device copy of known
+    size. A summary line looks like
+        traffic: kernel=K workload=W fetch_kib=F write_kib=X fetch_scale=a write_scale=b sources=D
+    None when no summary matches the current kernel sources."""
+    if not os.path.isdir(PROFILE_DIR):
+        return None
+    digest = kernel_sources_digest()
+    for f in sorted(os.listdir(PROFILE_DIR)):
+        if not f.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(PROFILE_DIR, f)) as fh:
+            for line in fh:
+                line = line.strip()
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(item.split("=", 1) for item in line[len("traffic:"):].split())
+                if kv.get("kernel") == kernel and kv.get("workload") == workload \
+                        and kv.get("sources") == digest:
+                    return 1024.0 * (float(kv["fetch_kib"]) * float(kv["fetch_scale"])
+                                     + float(kv["write_kib"]) * float(kv["write_scale"]))
+    return None
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, on a bounded sample: decode attention of the
     workload's decode requests at their first step, request after request."""
@@ -334,7 +377,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dom
     roof["avg_launch_us"] = 1e3 * kern[dom][1] / kern[dom][0]
-    roof["traffic"] = None
+    roof["algorithmic_bytes_per_launch"] = byt / (kern[dom][0] / args.steps)
+    roof["traffic"] = measured_traffic(dom, w.name)
+    roof["sources"] = kernel_sources_digest()
     # decode-phase aggregate HBM rate over all decode kernels' algorithmic bytes
     dec_bytes = sum(algorithmic(w, ep, n)[0] for n in ("decode_tail_valu", "segment_mfma",
                                                          "decode_fused", "mla_decode") if n in kern)

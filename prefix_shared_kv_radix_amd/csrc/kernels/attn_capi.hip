@@ -123,7 +123,17 @@ struct Profiler {
 };
 Profiler g_prof;
 
-// Brackets one launch with events on its stream while timing is enabled.
+}  // namespace
+
+namespace radix_launch {
+thread_local LaunchEvents g_launch_events;
+}
+
+namespace {
+
+// Times the one launch made in its scope while timing is enabled: the launch carries
+// the event pair, so the events hold the kernel's own start and end. A scope that
+// launches nothing records both events itself (zero duration).
 struct Timed {
   int32_t slot = -1;
   hipStream_t s;
@@ -131,11 +141,16 @@ struct Timed {
     if (g_prof.used < g_prof.cap) {
       slot = g_prof.used++;
       g_prof.ids[slot] = id;
-      hipEventRecord(g_prof.ev[2 * slot], s);
+      radix_launch::g_launch_events = {g_prof.ev[2 * slot], g_prof.ev[2 * slot + 1], false};
     }
   }
   ~Timed() {
-    if (slot >= 0) hipEventRecord(g_prof.ev[2 * slot + 1], s);
+    if (slot < 0) return;
+    if (!radix_launch::g_launch_events.used) {
+      hipEventRecord(g_prof.ev[2 * slot], s);
+      hipEventRecord(g_prof.ev[2 * slot + 1], s);
+    }
+    radix_launch::g_launch_events = {};
   }
 };
 

@@ -974,7 +974,7 @@ namespace radix_launch {
 
 hipError_t kv_store(const StoreArgs &a, int64_t T, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  kv_store_kernel<<<dim3(static_cast<unsigned>(T)), dim3(128), 0, stream>>>(a);
+  launch(kv_store_kernel, dim3(static_cast<unsigned>(T)), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -985,10 +985,10 @@ static hipError_t launch_valu(int mode, const AttnArgs &a, unsigned items, unsig
   if (waves > 0x7fffffffull) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
   const int n = static_cast<int>(items), ns = static_cast<int>(splits);
-  if (mode == 0) attn_valu_kernel<T, D, G, 0><<<grid, block, 0, stream>>>(a, n, ns);
-  else if (mode == 1) attn_valu_kernel<T, D, G, 1><<<grid, block, 0, stream>>>(a, n, ns);
-  else if (mode == 2) attn_valu_kernel<T, D, G, 2><<<grid, block, 0, stream>>>(a, n, ns);
-  else attn_valu_kernel<T, D, G, 3><<<grid, block, 0, stream>>>(a, n, ns);
+  if (mode == 0) launch(attn_valu_kernel<T, D, G, 0>, grid, block, 0, stream, a, n, ns);
+  else if (mode == 1) launch(attn_valu_kernel<T, D, G, 1>, grid, block, 0, stream, a, n, ns);
+  else if (mode == 2) launch(attn_valu_kernel<T, D, G, 2>, grid, block, 0, stream, a, n, ns);
+  else launch(attn_valu_kernel<T, D, G, 3>, grid, block, 0, stream, a, n, ns);
   return hipGetLastError();
 }
 
@@ -1011,8 +1011,8 @@ static hipError_t launch_tail(int mode, const AttnArgs &a, unsigned items, unsig
   if (waves > 0x7fffffffull) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
   const int n = static_cast<int>(items), ns = static_cast<int>(splits);
-  if (mode == 0) tail_bf16_kernel<G, 0><<<grid, block, 0, stream>>>(a, n, ns);
-  else tail_bf16_kernel<G, 3><<<grid, block, 0, stream>>>(a, n, ns);
+  if (mode == 0) launch(tail_bf16_kernel<G, 0>, grid, block, 0, stream, a, n, ns);
+  else launch(tail_bf16_kernel<G, 3>, grid, block, 0, stream, a, n, ns);
   return hipGetLastError();
 }
 
@@ -1038,8 +1038,8 @@ static hipError_t launch_mfma(bool seg, const AttnArgs &a, unsigned tiles, unsig
   const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
   if (n > 0x7fffffffull) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(256);
-  if (seg) attn_mfma_kernel<G, true><<<grid, block, 0, s>>>(a, tiles, items);
-  else attn_mfma_kernel<G, false><<<grid, block, 0, s>>>(a, tiles, items);
+  if (seg) launch(attn_mfma_kernel<G, true>, grid, block, 0, s, a, tiles, items);
+  else launch(attn_mfma_kernel<G, false>, grid, block, 0, s, a, tiles, items);
   return hipGetLastError();
 }
 
@@ -1049,8 +1049,8 @@ static hipError_t launch_fused(const AttnArgs &a, unsigned tiles, unsigned seg_i
   const uint64_t seg_blocks = 8 * ((static_cast<uint64_t>(tiles) * seg_items * a.Hkv + 7) / 8);
   const uint64_t tail_blocks = (static_cast<uint64_t>(n_items) * nsplit * a.Hkv + 3) / 4;
   if (seg_blocks + tail_blocks > 0x7fffffffull) return hipErrorInvalidValue;
-  decode_fused_kernel<G><<<dim3(static_cast<unsigned>(seg_blocks + tail_blocks)), dim3(256), 0, s>>>(
-      a, tiles, seg_items, n_items, nsplit);
+  launch(decode_fused_kernel<G>, dim3(static_cast<unsigned>(seg_blocks + tail_blocks)), dim3(256), 0,
+         s, a, tiles, seg_items, n_items, nsplit);
   return hipGetLastError();
 }
 
@@ -1081,8 +1081,8 @@ hipError_t mfma(int G, bool seg, const AttnArgs &a, int max_rows, unsigned items
 hipError_t combine(bool bf16, const AttnArgs &a, int batch, int Dv, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   dim3 grid(batch, a.Hq), block(128);
-  if (bf16) combine_kernel<uint16_t><<<grid, block, 0, s>>>(a, Dv);
-  else combine_kernel<float><<<grid, block, 0, s>>>(a, Dv);
+  if (bf16) launch(combine_kernel<uint16_t>, grid, block, 0, s, a, Dv);
+  else launch(combine_kernel<float>, grid, block, 0, s, a, Dv);
   return hipGetLastError();
 }
 

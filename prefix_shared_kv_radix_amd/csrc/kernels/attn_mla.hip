@@ -314,8 +314,8 @@ unsigned mla_blocks(const MlaArgs &a) {
 hipError_t mla(const MlaArgs &a, hipStream_t s) {
   const unsigned blocks = mla_blocks(a);
   if (blocks == 0) return hipSuccess;
-  if (a.fp8) mla_decode_kernel<true><<<dim3(blocks), dim3(512), 0, s>>>(a);
-  else mla_decode_kernel<false><<<dim3(blocks), dim3(512), 0, s>>>(a);
+  if (a.fp8) launch(mla_decode_kernel<true>, dim3(blocks), dim3(512), 0, s, a);
+  else launch(mla_decode_kernel<false>, dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
