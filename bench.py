@@ -118,7 +118,8 @@ class Episode:
                 self.max_ws = max(self.max_ws, _lib.decode_workspace_size(
                     d.shape, B, int(seq.max()), plan, splits))
             self.staged.append(st)
-        self.ws = torch.empty(max(self.max_ws // 4, 1), dtype=torch.float32, device=dev)
+        # zeroed once: the bf16 decode's merge counters must start at zero (calls leave them so)
+        self.ws = torch.zeros(max(self.max_ws // 4, 1), dtype=torch.float32, device=dev)
         self.rtt_pin = torch.empty((2, max_batch, self.stride), dtype=torch.int32, pin_memory=True)
         self.parity = 0
         self.done_evt = [None, None]
@@ -168,10 +169,15 @@ class Episode:
                     slots = tree.alloc(B)
                     rows[np.arange(B), st["prompt_len"] + s] = slots
                     pin[s].copy_(torch.from_numpy(slots))
-                    st["slot_dev"][s].copy_(pin[s], non_blocking=True)
+                    # GQA decode reads the new slots from pinned host memory (no copy launch);
+                    # the MLA path stores the new rows in a separate launch first, from device memory
+                    slot_arg = pin[s]
+                    if w.shape.v_is_k_prefix:
+                        st["slot_dev"][s].copy_(pin[s], non_blocking=True)
+                        slot_arg = st["slot_dev"][s]
                     _lib.attn_decode(d.shape, d.kv, st["dq"][s], st["dk"][s],
                                      None if st["dv"] is None else st["dv"][s],
-                                     None if st["dsc"] is None else st["dsc"][s], st["slot_dev"][s],
+                                     None if st["dsc"] is None else st["dsc"][s], slot_arg,
                                      d.rtt, None, st["seq_dev"][s], B, int(st["seq_host"][s].max()),
                                      plan_dev, self.splits, st["dout"], None, self.ws)
             if mark:

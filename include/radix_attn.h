@@ -295,8 +295,12 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
 
 /* Decode attention: request b's query (position seq_lens[b]-1) attends keys
  * 0 .. seq_lens[b]-1 read through req_to_token[row]. When new_slots is not NULL,
- * first req_to_token[row][seq_lens[b]-1] = new_slots[b] and the new K/V row
- * (k_new/v_new/scale_new dev [batch, Hkv, *]) is stored at that slot.
+ * req_to_token[row][seq_lens[b]-1] = new_slots[b] and the new K/V row
+ * (k_new/v_new/scale_new dev [batch, Hkv, *]) is stored at that slot; the query
+ * attends the new row itself (read from k_new/v_new). new_slots [batch] int32 may be
+ * device memory or pinned host memory mapped into the device (then no copy to the
+ * device is needed; the host must not change it until the call's work has run);
+ * any other pointer is E_INVAL.
  * With a plan, each shared segment's keys are read once for all its members and
  * keys from req_private_start[b] on are read per request; without a plan (NULL)
  * every request reads all its keys. A request's private keys are cut into
@@ -304,7 +308,12 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
  * tails are short and the batch fills the GPU, else 512-key chunks); all partial
  * results are merged exactly by their log-sum-exp.
  *   q dev [batch, Hq, Dqk]; out dev [batch, Hq, Dv]; lse_out dev [batch, Hq] or NULL;
- *   workspace dev, at least radix_attn_decode_workspace_size bytes.
+ *   workspace dev, at least radix_attn_decode_workspace_size bytes. bf16 K/V: the
+ *   partial results are merged inside the one decode launch by whichever block
+ *   finishes a request last, counted in the workspace's first 256 KiB (int32 per
+ *   request and KV head; batch * Hkv <= 65536, else E_INVAL); that region must be
+ *   zero before the first call on a workspace (e.g. allocate it zeroed) and every
+ *   call leaves it zero. A workspace serves one call at a time.
  *   max_seq_len: host bound on seq_lens (grid sizing). */
 radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buffers *kv,
                                const void *q, const void *k_new, const void *v_new,

@@ -69,6 +69,8 @@ struct AttnArgs {
   void *out;
   float *lse;
   float *ws_o, *ws_lse;
+  // bf16 decode: arrival counters [batch, Hkv] of the in-kernel merge (zero between calls)
+  int32_t *merge_cnt;
   int Hq, Hkv;
   float scale_log2;
 };
@@ -96,9 +98,14 @@ hipError_t mla(const MlaArgs &a, hipStream_t s);
 // 2: shared segment -> partial, 3: decode private tail -> final output (merges shared partials)
 hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, unsigned splits,
                 hipStream_t s);
-hipError_t mfma(int G, bool seg, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s);
+// extend attention with bf16 MFMA tiles (128 query rows x 64-key tiles)
+hipError_t mfma(int G, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s);
+// bf16 decode over the private keys of each request (split into `splits` chunks): output
+// written directly, or partials merged in-kernel by the last producer (merge_cnt)
+hipError_t decode_tail_bf16(int G, const AttnArgs &a, unsigned batch, unsigned splits, hipStream_t s);
 hipError_t combine(bool bf16, const AttnArgs &a, int batch, int Dv, hipStream_t s);
-// one launch: shared-segment MFMA tiles + private-tail waves, all writing partials
+// one launch: shared-segment MFMA tiles + private-tail waves; the last producer of each
+// (request, KV head) merges its partials (merge_cnt)
 hipError_t decode_fused(int G, const AttnArgs &a, int max_rows, unsigned seg_items,
                         unsigned n_items, unsigned nsplit, hipStream_t s);
 

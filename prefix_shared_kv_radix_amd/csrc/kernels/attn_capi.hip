@@ -147,12 +147,23 @@ struct Timed {
   ~Timed() {
     if (slot < 0) return;
     if (!radix_launch::g_launch_events.used) {
-      hipEventRecord(g_prof.ev[2 * slot], s);
-      hipEventRecord(g_prof.ev[2 * slot + 1], s);
+      (void)hipEventRecord(g_prof.ev[2 * slot], s);
+      (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
     }
     radix_launch::g_launch_events = {};
   }
 };
+
+// Launch-shape tuning (overridable at build time).
+#ifndef RADIX_SEG_BLOCKS
+#define RADIX_SEG_BLOCKS 256
+#endif
+#ifndef RADIX_TAIL_CHUNK
+#define RADIX_TAIL_CHUNK 512
+#endif
+#ifndef RADIX_TAIL_WAVES
+#define RADIX_TAIL_WAVES 2048
+#endif
 
 // Key splits per shared segment: enough blocks to fill the chip (~512 for the MFMA
 // segment kernel), at least 256 keys per split, at most 16 splits.
@@ -163,7 +174,7 @@ int seg_splits_for(const radix_attn_shape *s, const radix_decode_plan *plan) {
   const long rows = static_cast<long>(plan->max_members) * (mla ? 1 : G);
   const long tiles = mla ? rows : (rows + 127) / 128;
   const long blocks = tiles * plan->num_segments * s->num_kv_heads;
-  const long target = mla ? 1024 : 256;   // the segment tiles overlap the tail waves
+  const long target = mla ? 1024 : RADIX_SEG_BLOCKS;   // the segment tiles overlap the tail waves
   long ss = (target + blocks - 1) / (blocks > 0 ? blocks : 1);
   const long cap = plan->max_seg_len / 256 > 1 ? plan->max_seg_len / 256 : 1;
   if (ss > cap) ss = cap;
@@ -174,9 +185,9 @@ int seg_splits_for(const radix_attn_shape *s, const radix_decode_plan *plan) {
 // Private-tail chunking: one chunk per request when the tails are short and the batch
 // alone gives ~2048 waves; otherwise 512-key chunks (more for very long tails), so
 // requests of very different lengths still spread evenly over the GPU.
-constexpr int kTailChunk = 512;
+constexpr int kTailChunk = RADIX_TAIL_CHUNK;
 int auto_splits(int batch, int hkv, int private_len) {
-  if (private_len <= 2 * kTailChunk && batch * hkv >= 2048) return 1;
+  if (private_len <= 2 * kTailChunk && batch * hkv >= RADIX_TAIL_WAVES) return 1;
   int s = (private_len + kTailChunk - 1) / kTailChunk;
   if (s > 64) s = 64;
   return s < 1 ? 1 : s;
@@ -195,6 +206,32 @@ int private_len_bound(int max_seq_len, const radix_decode_plan *plan) {
   const bool use_plan = plan && plan->num_segments > 0;
   const int p = max_seq_len - (use_plan ? plan->min_private_start : 0);
   return p < 1 ? 1 : p;
+}
+
+// True if the kernels may read p: device memory, or host memory pinned and mapped into
+// the device's address space at the same address (a pageable pointer would fault).
+bool device_readable(const void *p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error of the failed query
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return true;
+  return at.type == hipMemoryTypeHost && at.devicePointer == p;
+}
+
+// bf16 decode workspace: arrival counters of the in-kernel merge at a fixed place (the
+// first 256 KiB, one int32 per (request, KV head)), so a workspace reused by calls of
+// other shapes never finds partial data where counters are expected; partials follow.
+constexpr int64_t kMergeCounters = 1 << 16;
+constexpr size_t kMergeCounterBytes = kMergeCounters * sizeof(int32_t);
+
+// partial outputs [batch, Hq, parts, Dv] and their lse [batch, Hq, parts], fp32, rounded
+// up to 256 bytes
+size_t partials_bytes(const radix_attn_shape *shape, int32_t batch, size_t parts) {
+  const size_t b = static_cast<size_t>(batch) * shape->num_q_heads * parts *
+                   (static_cast<size_t>(shape->head_dim_v) + 1) * sizeof(float);
+  return (b + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -259,8 +296,9 @@ radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int
     *bytes = 0;  // single pass, nothing to merge
     return RADIX_OK;
   }
-  *bytes = static_cast<size_t>(batch) * shape->num_q_heads * parts *
-           (static_cast<size_t>(shape->head_dim_v) + 1) * sizeof(float);
+  // bf16: the in-kernel merge's arrival counters occupy a fixed region in front
+  *bytes = (shape->q_dtype == RADIX_BF16 ? kMergeCounterBytes : 0) +
+           partials_bytes(shape, batch, parts);
   return RADIX_OK;
 }
 
@@ -303,7 +341,7 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (classify(shape) == Kind::GqaBf16) {
     Timed t(K_EXTEND_MFMA, s);
-    return hip_status(radix_launch::mfma(G, false, a, max_extend * G, batch, s), "extend launch");
+    return hip_status(radix_launch::mfma(G, a, max_extend * G, batch, s), "extend launch");
   }
   Timed t(K_EXTEND_VALU, s);
   return hip_status(radix_launch::valu(false, G, 1, a, total_extend, 1, s), "extend launch");
@@ -326,6 +364,8 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   REQUIRE(max_seq_len >= 1 && max_seq_len <= rtt_stride, "max_seq_len outside [1, rtt_stride]");
   REQUIRE(!k_new || shape->v_is_k_prefix || v_new, "missing new V rows");
   REQUIRE(!k_new || shape->kv_dtype != RADIX_FP8_E4M3 || scale_new, "missing new fp8 scales");
+  REQUIRE(!new_slots || device_readable(new_slots),
+          "new_slots must be device memory or pinned (device-mapped) host memory");
   const bool use_plan = plan && plan->num_segments > 0;
   if (use_plan) {
     REQUIRE(plan->seg_row && plan->seg_start && plan->seg_end && plan->seg_member_off &&
@@ -400,7 +440,11 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   size_t need = 0;
   radix_attn_decode_workspace_size(shape, batch, max_seq_len, plan, splits, &need);
   REQUIRE(direct || (workspace && workspace_bytes >= need), "decode workspace too small");
-  float *ws_o = direct ? nullptr : static_cast<float *>(workspace);
+  REQUIRE(direct || kind != Kind::GqaBf16 ||
+              static_cast<int64_t>(batch) * shape->num_kv_heads <= kMergeCounters,
+          "batch * num_kv_heads above the merge counter capacity (65536)");
+  char *ws_parts = static_cast<char *>(workspace) + (kind == Kind::GqaBf16 ? kMergeCounterBytes : 0);
+  float *ws_o = direct ? nullptr : reinterpret_cast<float *>(ws_parts);
   float *ws_lse = direct ? nullptr
                          : ws_o + static_cast<size_t>(batch) * shape->num_q_heads * parts *
                                       shape->head_dim_v;
@@ -433,43 +477,43 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     a.num_segments = plan->num_segments;
     a.req_num_shared = plan->req_num_shared;
     a.private_start = plan->req_private_start;
-    if (bf16) {
-      // one launch: segment tiles and private-tail waves, then the merge
-      {
-        Timed t(K_DECODE_FUSED, s);
-        st = hip_status(radix_launch::decode_fused(
+  }
+  if (bf16) {
+    // one launch per step: partials are merged in-kernel by their last producer
+    a.merge_cnt = direct ? nullptr : static_cast<int32_t *>(workspace);
+    Timed t(use_plan ? K_DECODE_FUSED : K_DECODE_TAIL, s);
+    if (use_plan)
+      return hip_status(radix_launch::decode_fused(
                             G, a, plan->max_members * G,
                             static_cast<unsigned>(plan->num_segments * seg_splits),
                             static_cast<unsigned>(batch), static_cast<unsigned>(splits), s),
                         "decode launch");
-      }
-      if (st != RADIX_OK) return st;
-      Timed t(K_COMBINE, s);
-      return hip_status(radix_launch::combine(bf16, a, batch, shape->head_dim_v, s),
-                        "combine launch");
-    } else {
-      Timed t(K_SEGMENT_VALU, s);
-      st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, seg_splits, s),
-                      "segment launch");
-    }
+    return hip_status(radix_launch::decode_tail_bf16(G, a, static_cast<unsigned>(batch),
+                                                     static_cast<unsigned>(splits), s),
+                      "decode launch");
+  }
+  if (use_plan) {
+    Timed t(K_SEGMENT_VALU, s);
+    st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, seg_splits, s),
+                    "segment launch");
     if (st != RADIX_OK) return st;
   }
   if (splits == 1) {
     Timed t(K_DECODE_TAIL, s);
-    return hip_status(radix_launch::valu(bf16, G, 3, a, batch, 1, s), "decode launch");
+    return hip_status(radix_launch::valu(false, G, 3, a, batch, 1, s), "decode launch");
   }
   {
     Timed t(K_DECODE_TAIL, s);
-    st = hip_status(radix_launch::valu(bf16, G, 0, a, batch, splits, s), "decode launch");
+    st = hip_status(radix_launch::valu(false, G, 0, a, batch, splits, s), "decode launch");
   }
   if (st != RADIX_OK) return st;
   Timed t(K_COMBINE, s);
-  return hip_status(radix_launch::combine(bf16, a, batch, shape->head_dim_v, s), "combine launch");
+  return hip_status(radix_launch::combine(false, a, batch, shape->head_dim_v, s), "combine launch");
 }
 
 radix_status radix_profile_enable(int32_t capacity) {
   REQUIRE(capacity >= 0, "negative profiling capacity");
-  for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
   g_prof.ev.clear();
   g_prof.ids.assign(capacity, 0);
   g_prof.cap = 0;
@@ -478,7 +522,7 @@ radix_status radix_profile_enable(int32_t capacity) {
     hipEvent_t e;
     hipError_t err = hipEventCreate(&e);
     if (err != hipSuccess) {
-      for (hipEvent_t x : g_prof.ev) hipEventDestroy(x);
+      for (hipEvent_t x : g_prof.ev) (void)hipEventDestroy(x);
       g_prof.ev.clear();
       return hip_status(err, "hipEventCreate");
     }

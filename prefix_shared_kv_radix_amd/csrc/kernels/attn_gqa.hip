@@ -113,12 +113,14 @@ template <> struct Vec16<uint16_t> {
   }
 };
 
-template <typename T> __device__ __forceinline__ void store_out(void *out, int64_t idx, float v);
-template <> __device__ __forceinline__ void store_out<float>(void *out, int64_t idx, float v) {
-  reinterpret_cast<float *>(out)[idx] = v;
+// four consecutive values at idx (a multiple of 4)
+template <typename T> __device__ __forceinline__ void store_out4(void *out, int64_t idx, f32x4 v);
+template <> __device__ __forceinline__ void store_out4<float>(void *out, int64_t idx, f32x4 v) {
+  *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + idx) = v;
 }
-template <> __device__ __forceinline__ void store_out<uint16_t>(void *out, int64_t idx, float v) {
-  reinterpret_cast<uint16_t *>(out)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+template <> __device__ __forceinline__ void store_out4<uint16_t>(void *out, int64_t idx, f32x4 v) {
+  *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(out) + idx) =
+      u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
@@ -398,9 +400,13 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int n_items,
 //          permutes, v_dot2_f32_bf16 per dim (fp32 accumulation)
 // The running maximum is refreshed only when some head's tile maximum exceeds it by
 // more than 2^8 (numerator and denominator share the stale maximum, so nothing is lost).
-// MODE 0 writes a partial; MODE 3 writes the output, merged with the request's
-// shared-segment partials. The newest key is read from k_new/v_new when given and the
-// chunk-0 wave stores it and appends its slot.
+// A request whose keys all fall in this one chunk (no shared segment, one chunk) writes
+// its output directly. Otherwise the wave writes a partial and arrives at the request's
+// merge counter; whichever producer of the request arrives last (this wave, another
+// chunk, or a shared-segment tile) merges every partial into the output, so no second
+// launch is needed. The newest key is read from k_new/v_new; the chunk-0 wave stores it
+// at its slot and appends the slot to the slot list after its own loop (no other wave
+// of this launch reads that slot or list entry).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
@@ -419,16 +425,74 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
+// Merges every partial of request b for the G query heads of KV head kvh into the
+// bf16 output (and lse): lane -> 8 dims of one head, 512 values per pass. Partials of
+// shared segments come first ([0, req_num_shared[b] * seg_splits)), then the private
+// chunks ([part_base, part_base + num_splits)); an empty partial has lse -inf and
+// weight 0. Called by the last producer to arrive, after its counter read.
+template <int G>
+__device__ __forceinline__ void merge_request_bf16(const AttnArgs &a, int b, int kvh) {
+  const int lane = threadIdx.x & 63;
+  const int ns = a.req_num_shared ? a.req_num_shared[b] * a.seg_splits : 0;
+  const int total = ns + a.num_splits;
+#pragma unroll
+  for (int c = 0; c < (G * 128 + 511) / 512; ++c) {
+    const int e = c * 512 + lane * 8;
+    if (e >= G * 128) break;
+    const int head = kvh * G + e / 128, d = e % 128;
+    const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
+    float M = kNegBig, L = 0.f;
+    f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = O0;
+    for (int p0 = 0; p0 < total; p0 += 4) {
+      float pl[4];
+      f32x4 pa[4], pb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = p0 + j;
+        const int64_t pi = base + (idx < ns ? idx : a.part_base + idx - ns);
+        const bool ok = idx < total;
+        pl[j] = ok ? ld_dev1(a.ws_lse + pi) : -INFINITY;
+        pa[j] = ok ? ld_dev(a.ws_o + pi * 128 + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+        pb[j] = ok ? ld_dev(a.ws_o + pi * 128 + d + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float mx = M;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, pl[j]);
+      const float alpha = exp2f(M - mx);
+      L *= alpha;
+      O0 *= alpha;
+      O1 *= alpha;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float wj = exp2f(pl[j] - mx);
+        L += wj;
+        if (wj > 0.f) {
+          O0 += pa[j] * wj;
+          O1 += pb[j] * wj;
+        }
+      }
+      M = mx;
+    }
+    const float inv = 1.f / L;
+    uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + (static_cast<int64_t>(b) * a.Hq + head) * 128 + d;
+    *reinterpret_cast<u32x4 *>(op) =
+        u32x4{pack2bf(O0[0] * inv, O0[1] * inv), pack2bf(O0[2] * inv, O0[3] * inv),
+              pack2bf(O1[0] * inv, O1[1] * inv), pack2bf(O1[2] * inv, O1[3] * inv)};
+    if (a.lse && d == 0) a.lse[static_cast<int64_t>(b) * a.Hq + head] = (M + log2f(L)) * kLn2;
+  }
+}
+
 #ifndef RADIX_TAIL_STAGES
 #define RADIX_TAIL_STAGES 3
 #endif
 
-template <int G, int MODE>
+template <int G>
 __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_items, int nsplit) {
   constexpr int D = 128;
   constexpr int NB = RADIX_TAIL_STAGES;
   constexpr float kGrow = 8.f;
   const int lane = threadIdx.x & 63, r8 = lane >> 3, sub = lane & 7;
+  w = __builtin_amdgcn_readfirstlane(w);   // one work item per wave: its indices are scalar
   if (w >= n_items * nsplit * a.Hkv) return;
   const int kvh = w % a.Hkv;
   const int split = (w / a.Hkv) % nsplit;
@@ -448,22 +512,18 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * 2 + sub * 32;
   const bool fuse_new = a.k_new != nullptr;
   const char *knew = nullptr, *vnew = nullptr;
+  // the new token's slot: read now (new_slots may be pinned host memory), used at the end
+  const bool store_new = fuse_new && split == 0;
+  const int64_t new_at = static_cast<int64_t>(a.req_rows ? a.req_rows[b] : b) * a.rtt_stride + hi - 1;
+  int32_t new_slot = 0;
   if (fuse_new) {
     const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D * 2 + sub * 32;
     knew = reinterpret_cast<const char *>(a.k_new) + off;
     vnew = reinterpret_cast<const char *>(a.v_new) + off;
-    if (split == 0 && r8 == 0) {
-      const int64_t at = static_cast<int64_t>(a.req_rows ? a.req_rows[b] : b) * a.rtt_stride + hi - 1;
-      const int64_t slot = a.new_slots ? a.new_slots[b] : a.rtt[at];
-      if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[at] = static_cast<int32_t>(slot);
-      char *kd = const_cast<char *>(kb) + slot * row_bytes;
-      char *vd = const_cast<char *>(vb) + slot * row_bytes;
-      *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
-      *reinterpret_cast<u32x4 *>(kd + 16) = ldg16(knew + 16);
-      *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
-      *reinterpret_cast<u32x4 *>(vd + 16) = ldg16(vnew + 16);
-    }
+    if (store_new) new_slot = a.new_slots ? a.new_slots[b] : a.rtt[new_at];
   }
+  const int ns_b = a.req_num_shared ? a.req_num_shared[b] * a.seg_splits : 0;
+  const int expected = ns_b + nsplit;   // producers of this request's output
 
   // q: G heads x this lane's 16 dims, packed bf16 pairs (unscaled)
   uint32_t qp[G][8];
@@ -488,38 +548,35 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
   }
 
-  // iteration t covers rows base .. base+15; this lane takes rows base + r8 and base + 8 + r8.
-  // Rows past the chunk point at a finite stored row (the newest key when fused, else the
-  // chunk's last row), so no masking of V is needed: their weight is exactly 0.
-  const int last = s_hi - 1;
+  // Pool rows of this chunk: [s_lo, pool_hi); the newest key (position hi-1, not yet in
+  // the pool when fused) is folded in once after the loop from k_new/v_new.
+  // Iteration t covers rows base .. base+15; this lane takes rows base + r8 and
+  // base + 8 + r8. Every load is unconditional: rows past pool_hi re-read the chunk's
+  // last pool row (finite, stored), and their weight is exactly 0.
+  const int pool_hi = fuse_new ? min(s_hi, hi - 1) : s_hi;
+  const int last = pool_hi - 1;
   u32x4 kbuf[NB][2][2], vbuf[NB][2][2];
   int32_t sbuf[NB][2];
   auto load_slots = [&](int base, int32_t *sl) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int r = base + 8 * g + r8;
-      const int32_t v = rtt_row[min(r, last)];
-      sl[g] = v;
-    }
+    for (int g = 0; g < 2; ++g) sl[g] = rtt_row[min(base + 8 * g + r8, last)];
   };
-  auto load_kv = [&](int base, const int32_t *sl, u32x4 (*kd)[2], u32x4 (*vd)[2]) {
+  auto load_kv = [&](const int32_t *sl, u32x4 (*kd)[2], u32x4 (*vd)[2]) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int r = base + 8 * g + r8;
-      const bool use_new = fuse_new && (r >= hi - 1 || r >= s_hi);
-      const char *kp = use_new ? knew : kb + static_cast<int64_t>(sl[g]) * row_bytes;
-      const char *vp = use_new ? vnew : vb + static_cast<int64_t>(sl[g]) * row_bytes;
+      const char *kp = kb + static_cast<int64_t>(sl[g]) * row_bytes;
+      const char *vp = vb + static_cast<int64_t>(sl[g]) * row_bytes;
       kd[g][0] = ldg16(kp);
       kd[g][1] = ldg16(kp + 16);
       vd[g][0] = ldg16(vp);
       vd[g][1] = ldg16(vp + 16);
     }
   };
-  auto compute = [&](int base, const u32x4 (*kr)[2], const u32x4 (*vr)[2]) {
+  auto compute = [&](bool valid0, bool valid1, const u32x4 (*kr)[2], const u32x4 (*vr)[2]) {
     float s[2][G];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const bool valid = base + 8 * g + r8 < s_hi;
+      const bool valid = g == 0 ? valid0 : valid1;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
@@ -539,7 +596,7 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float mn = fmaxf(m[h], fmaxf(s[0][h], s[1][h]));
-        const float alpha = exp2f(m[h] - mn);
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
         m[h] = mn;
         l[h] *= alpha;
 #pragma unroll
@@ -549,7 +606,8 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     uint32_t pp[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float p0 = exp2f(s[0][h] - m[h]), p1 = exp2f(s[1][h] - m[h]);
+      const float p0 = __builtin_amdgcn_exp2f(s[0][h] - m[h]);
+      const float p1 = __builtin_amdgcn_exp2f(s[1][h] - m[h]);
       l[h] += p0 + p1;
       pp[h] = pack2bf(p0, p1);
     }
@@ -567,21 +625,40 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     }
   };
 
+  // Step t computes iteration t (buffer t % NB). Before that it issues, in this order,
+  // the slot indices of iteration t+NB and the K/V rows of iteration t+NB-1 (whose slots
+  // came one step earlier). Loads return in issue order, so waiting for those slots
+  // never waits for the K/V rows issued one step earlier: NB-1 iterations stay in flight.
+  // The last group of NB steps runs whole (steps past the end are fully masked): an
+  // early exit inside it makes the compiler rotate the ring through registers that still
+  // have loads in flight, which costs a wait for them every step.
+  if (pool_hi > s_lo) {   // (uniform) no pool rows: nothing to load
 #pragma unroll
-  for (int j = 0; j < NB; ++j) load_slots(s_lo + 16 * j, sbuf[j]);
+    for (int j = 0; j < NB; ++j) load_slots(s_lo + 16 * j, sbuf[j]);
 #pragma unroll
-  for (int j = 0; j + 1 < NB; ++j) load_kv(s_lo + 16 * j, sbuf[j], kbuf[j], vbuf[j]);
-  for (int base = s_lo; base < s_hi; base += 16 * NB) {
+    for (int j = 0; j + 1 < NB; ++j) load_kv(sbuf[j], kbuf[j], vbuf[j]);
+    for (int base = s_lo; base < pool_hi; base += 16 * NB) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int it = base + 16 * j;
-      if (it >= s_hi) break;
-      const int jl = (j + NB - 1) % NB;
-      const int ahead = it + 16 * (NB - 1);
-      load_slots(ahead + 16, sbuf[j]);
-      load_kv(ahead, sbuf[jl], kbuf[jl], vbuf[jl]);
-      compute(it, kbuf[j], vbuf[j]);
+      for (int j = 0; j < NB; ++j) {
+        const int it = base + 16 * j;
+        const int jl = (j + NB - 1) % NB;
+        load_slots(it + 16 * NB, sbuf[j]);
+        load_kv(sbuf[jl], kbuf[jl], vbuf[jl]);
+        compute(it + r8 < pool_hi, it + 8 + r8 < pool_hi, kbuf[j], vbuf[j]);
+      }
     }
+  }
+  if (fuse_new && hi - 1 >= s_lo && hi - 1 < s_hi) {   // (uniform) the newest key
+    u32x4 kr[2][2], vr[2][2];
+    kr[0][0] = ldg16(knew);
+    kr[0][1] = ldg16(knew + 16);
+    vr[0][0] = ldg16(vnew);
+    vr[0][1] = ldg16(vnew + 16);
+    kr[1][0] = kr[0][0];
+    kr[1][1] = kr[0][1];
+    vr[1][0] = vr[0][0];
+    vr[1][1] = vr[0][1];
+    compute(r8 == 0, false, kr, vr);
   }
 
   // merge the 8 row groups (lanes l, l^8, l^16, l^32 hold the same dims)
@@ -599,8 +676,18 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     }
   }
 
+  if (store_new && r8 == 0) {
+    if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[new_at] = new_slot;
+    char *kd = const_cast<char *>(kb) + static_cast<int64_t>(new_slot) * row_bytes;
+    char *vd = const_cast<char *>(vb) + static_cast<int64_t>(new_slot) * row_bytes;
+    *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
+    *reinterpret_cast<u32x4 *>(kd + 16) = ldg16(knew + 16);
+    *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
+    *reinterpret_cast<u32x4 *>(vd + 16) = ldg16(vnew + 16);
+  }
+
   // group r8 writes (head, half) pairs r8, r8 + 8, ...: 8 dims each
-  const int nshared = (MODE == 3 && a.req_num_shared) ? a.req_num_shared[b] * a.seg_splits : 0;
+  const bool direct = expected == 1;
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -608,41 +695,14 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
       if (((2 * h + half) & 7) != r8) continue;
       const int head = kvh * G + h;
       const int d0 = sub * 16 + half * 8;
-      float M = m[h], L = l[h];
+      const float M = m[h], L = l[h];
       float O[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) O[e] = acc[h][half * 8 + e];
-      if (MODE == 3) {
-        const int64_t hp = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
-        for (int p0 = 0; p0 < nshared; p0 += 4) {
-          float pl[4];
-          f32x4 po[4][2];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bool ok = p0 + j < nshared;
-            pl[j] = ok ? a.ws_lse[hp + p0 + j] : -INFINITY;
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              po[j][c] = ok ? *reinterpret_cast<const f32x4 *>(a.ws_o + (hp + p0 + j) * D + d0 + 4 * c)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float mn = fmaxf(M, pl[j]);
-            const float wa = exp2f(M - mn), wb = exp2f(pl[j] - mn);
-            L = L * wa + wb;
-            M = mn;
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) O[4 * c + e] = O[4 * c + e] * wa + po[j][c][e] * wb;
-          }
-        }
-      }
       const bool empty = !(L > 0.f);
       const float inv = empty ? 0.f : 1.f / L;
       const float lse2 = empty ? -INFINITY : M + log2f(L);
-      if (MODE == 3) {
+      if (direct) {
         uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + (q_row * a.Hq + head) * D + d0;
         *reinterpret_cast<u32x4 *>(op) = u32x4{pack2bf(O[0] * inv, O[1] * inv), pack2bf(O[2] * inv, O[3] * inv),
                                                pack2bf(O[4] * inv, O[5] * inv), pack2bf(O[6] * inv, O[7] * inv)};
@@ -650,16 +710,27 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
       } else {
         const int64_t pi = (static_cast<int64_t>(b) * a.Hq + head) * a.parts + part;
         float *wp = a.ws_o + pi * D + d0;
-        *reinterpret_cast<f32x4 *>(wp) = f32x4{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
-        *reinterpret_cast<f32x4 *>(wp + 4) = f32x4{O[4] * inv, O[5] * inv, O[6] * inv, O[7] * inv};
-        if (d0 == 0) a.ws_lse[pi] = lse2;
+        st_dev(wp, f32x4{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv});
+        st_dev(wp + 4, f32x4{O[4] * inv, O[5] * inv, O[6] * inv, O[7] * inv});
+        if (d0 == 0) st_dev1(a.ws_lse + pi, lse2);
       }
     }
+  if (direct) return;
+  // arrive; the last producer merges (uniform branch: one counter per wave)
+  wait_stores();
+  int32_t *cnt = a.merge_cnt + static_cast<int64_t>(b) * a.Hkv + kvh;
+  int before = 0;
+  if (lane == 0) before = arrive(cnt);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before == expected - 1) {
+    if (lane == 0) reset_counter(cnt);
+    merge_request_bf16<G>(a, b, kvh);
+  }
 }
 
-template <int G, int MODE>
+template <int G>
 __global__ __launch_bounds__(256) void tail_bf16_kernel(AttnArgs a, int n_items, int nsplit) {
-  tail_bf16_body<G, MODE>(a, blockIdx.x * 4 + (threadIdx.x >> 6), n_items, nsplit);
+  tail_bf16_body<G>(a, blockIdx.x * 4 + (threadIdx.x >> 6), n_items, nsplit);
 }
 
 // ------------------------------------------------------------------ MFMA kernel
@@ -672,13 +743,6 @@ constexpr int MF_TILE = MF_BN * MF_D * 2;   // bytes of one K (or V) tile: 64 ro
 // within 128-byte halves so rows read at the same column hit different LDS banks.
 __device__ __forceinline__ int mf_swz(int r, int c) { return r * 256 + ((c ^ (r & 7)) << 4); }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) s16x4 *>(
-          reinterpret_cast<uintptr_t>(p)));
-  return __builtin_bit_cast(u32x2, v);
-}
 
 __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void *>(
@@ -755,7 +819,14 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+  // running max of the scaled scores (log2 domain) and the row sum; the max is kept
+  // stale until a tile's maximum exceeds it by more than 2^8 (numerator and denominator
+  // share it, so the result is the same and the accumulators are rarely rescaled)
   float m_run = kNegBig, l_run = 0.f;
+  const float sc = a.scale_log2;   // > 0
+  // first query position among this wave's rows: tiles wholly at or before it need no
+  // causal mask (wave-uniform)
+  const int wave_q0 = SEG ? 0x7fffffff : P + (tile * MF_BM + wave * 32) / G;
 
   // loaders: wave w fills rows 16w .. 16w+15 of each tile, 4 rows per instruction;
   // lane i lands at byte 16*i of the instruction's 1 KB, i.e. row +i/16, physical chunk
@@ -807,34 +878,39 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
         st[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], st[mb], 0, 0, 0);
       }
     }
-    float mx = kNegBig;
+    if (kt + MF_BN > hi || kt + MF_BN - 1 > wave_q0) {   // (wave-uniform) ragged or diagonal tile
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt + mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          st[mb][i] = (key < hi && key <= qpos) ? st[mb][i] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kt + mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        float v = st[mb][i] * a.scale_log2;
-        v = (key < hi && key <= qpos) ? v : -INFINITY;
-        st[mb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, xor32(mx));
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - mn);
-    m_run = mn;
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(st[mb][i], st[mb][i + 1]));
+    mx = fmaxf(mx, xor32(mx)) * sc;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] *= alpha;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(st[mb][i] - mn);
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[mb][i], sc, -m_run));
         st[mb][i] = p;
         rs += p;
       }
-    rs += xor32(rs);
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] *= alpha;
+    l_run += rs + xor32(rs);
 
     bf16x8 pb[2][2];
 #pragma unroll
@@ -844,7 +920,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          w[e] = pack_bf16x2(st[mb][8 * j + 2 * e], st[mb][8 * j + 2 * e + 1]);
+          w[e] = pack2bf(st[mb][8 * j + 2 * e], st[mb][8 * j + 2 * e + 1]);
         pb[mb][j] = __builtin_bit_cast(bf16x8, w);
       }
     // V^T operand: in each 16-lane group g, source lane s reads 4 dims of key row
@@ -852,27 +928,32 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     // 4 keys of value dim 16*(g&1) + s of the 32-dim block.
     const int g = lane >> 4, s16 = lane & 15;
     const int vrow0 = 4 * (g >> 1) + (s16 >> 2);
+    const uint32_t vbase = lds_addr(Vt);
 #pragma unroll
     for (int dvb = 0; dvb < 4; ++dvb) {
       const int dv0 = dvb * 32 + 16 * (g & 1) + 4 * (s16 & 3);
       const int c = dv0 >> 3, half = (dv0 >> 2) & 1;
+      uint32_t ad[8];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int q = 0; q < 4; ++q) {   // q = 2 * mb + j: keys 16q .. 16q+15 of the tile
+        const int r0 = 16 * q + vrow0;
+        ad[2 * q] = vbase + mf_swz(r0, c) + 8 * half;
+        ad[2 * q + 1] = vbase + mf_swz(r0 + 8, c) + 8 * half;
+      }
+      u32x2 rv[8];
+      lds_tr16_x8(rv, ad);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r0 = mb * 32 + 16 * j + vrow0;
-          const u32x2 lo2 = lds_tr16(Vt + mf_swz(r0, c) + 8 * half);
-          const u32x2 hi2 = lds_tr16(Vt + mf_swz(r0 + 8, c) + 8 * half);
-          const u32x4 w = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-          o[dvb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[mb][j],
-                                                           o[dvb], 0, 0, 0);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 w = u32x4{rv[2 * q][0], rv[2 * q][1], rv[2 * q + 1][0], rv[2 * q + 1][1]};
+        o[dvb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
+                                                         pb[q >> 1][q & 1], o[dvb], 0, 0, 0);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  if (!rvalid) return;
+  if (!SEG && !rvalid) return;
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse2 = empty ? -INFINITY : m_run + log2f(l_run);
@@ -889,19 +970,40 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       }
     if (a.lse && h == 0) a.lse[q_tok * a.Hq + head] = lse2 * kLn2;
   } else {
-    const int part = a.seg_member_slot[mem_off + qi] * a.seg_splits + item % a.seg_splits;
-    const int64_t pi = (q_tok * a.Hq + head) * a.parts + part;
-    float *wp = a.ws_o + pi * MF_D;
+    // partial of this key range for every member row, then one arrival per member
+    // request (its head-0 lane); a member whose other producers have all arrived is
+    // merged here by the whole wave
+    int last_b = -1;
+    if (rvalid) {
+      const int part = a.seg_member_slot[mem_off + qi] * a.seg_splits + item % a.seg_splits;
+      const int64_t pi = (q_tok * a.Hq + head) * a.parts + part;
+      float *wp = a.ws_o + pi * MF_D;
 #pragma unroll
-    for (int dvb = 0; dvb < 4; ++dvb)
+      for (int dvb = 0; dvb < 4; ++dvb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dv = dvb * 32 + 8 * g4 + 4 * h;
-        *reinterpret_cast<f32x4 *>(wp + dv) =
-            f32x4{o[dvb][4 * g4] * inv, o[dvb][4 * g4 + 1] * inv, o[dvb][4 * g4 + 2] * inv,
-                  o[dvb][4 * g4 + 3] * inv};
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dv = dvb * 32 + 8 * g4 + 4 * h;
+          st_dev(wp + dv, f32x4{o[dvb][4 * g4] * inv, o[dvb][4 * g4 + 1] * inv,
+                                o[dvb][4 * g4 + 2] * inv, o[dvb][4 * g4 + 3] * inv});
+        }
+      if (h == 0) st_dev1(a.ws_lse + pi, lse2);
+    }
+    wait_stores();
+    if (rvalid && hg == 0 && h == 0) {
+      const int bq = static_cast<int>(q_tok);
+      const int expected = a.req_num_shared[bq] * a.seg_splits + a.num_splits;
+      int32_t *cnt = a.merge_cnt + static_cast<int64_t>(bq) * a.Hkv + kvh;
+      if (arrive(cnt) == expected - 1) {
+        reset_counter(cnt);
+        last_b = bq;
       }
-    if (h == 0) a.ws_lse[pi] = lse2;
+    }
+    uint64_t pending = __builtin_amdgcn_ballot_w64(last_b >= 0);
+    while (pending) {
+      const int l = __builtin_ctzll(pending);
+      pending &= pending - 1;
+      merge_request_bf16<G>(a, __builtin_amdgcn_readlane(last_b, l), kvh);
+    }
   }
 }
 
@@ -912,14 +1014,14 @@ __device__ __forceinline__ int xcd_logical(int bid, int nblocks) {
   return (bid & 7) * per + (bid >> 3);
 }
 
-// logical block -> (tile, item, kvh), tile fastest
-template <int G, bool SEG>
+// extend: logical block -> (tile, request, kvh), tile fastest
+template <int G>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
   const int nblocks = tiles * items * a.Hkv;
   const int lb = xcd_logical(blockIdx.x, nblocks);
   if (lb >= nblocks) return;
-  mfma_body<G, SEG>(a, lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
+  mfma_body<G, false>(a, lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
 }
 
 // One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
@@ -936,35 +1038,60 @@ __global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int ti
     if (lb >= nblocks) return;
     mfma_body<G, true>(a, lb % tiles, (lb / tiles) % seg_items, lb / (tiles * seg_items), smem);
   } else {
-    tail_bf16_body<G, 0>(a, (blockIdx.x - seg_blocks) * 4 + (threadIdx.x >> 6), n_items, nsplit);
+    tail_bf16_body<G>(a, (blockIdx.x - seg_blocks) * 4 + (threadIdx.x >> 6), n_items, nsplit);
   }
 }
 
 // ------------------------------------------------------------------ combine
+// Merges the partials of every (request, head) into the output. One wave covers 256
+// consecutive values of a request's [Hq, Dv] output (lane: 4 dims of one head); the
+// partials are taken 8 at a time with all their loads issued before any is used, and
+// folded into a running (M, L, O) in the log2 domain. An empty partial has lse -inf and
+// weight exactly 0 (its stored values are not read into the sum).
 template <typename T>
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a, int Dv) {
-  const int b = blockIdx.x, head = blockIdx.y;
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int Dv, int batch) {
+  const int lane = threadIdx.x & 63;
+  const int per_req = (a.Hq * Dv + 255) / 256;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= batch * per_req) return;
+  const int b = w / per_req;
+  const int e = (w % per_req) * 256 + lane * 4;
+  if (e >= a.Hq * Dv) return;
+  const int head = e / Dv, d = e % Dv;
   const int ns = a.req_num_shared ? a.req_num_shared[b] * a.seg_splits : 0;
+  const int total = ns + a.num_splits;
   const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
-  float M = -INFINITY;
-  for (int p = 0; p < ns; ++p) M = fmaxf(M, a.ws_lse[base + p]);
-  for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, a.ws_lse[base + a.part_base + s]);
-  float L = 0.f;
-  for (int p = 0; p < ns; ++p) L += exp2f(a.ws_lse[base + p] - M);
-  for (int s = 0; s < a.num_splits; ++s) L += exp2f(a.ws_lse[base + a.part_base + s] - M);
-  const float inv = 1.f / L;
-  for (int d = threadIdx.x; d < Dv; d += blockDim.x) {
-    float o = 0.f;
-    for (int p = 0; p < ns; ++p)
-      o = fmaf(exp2f(a.ws_lse[base + p] - M), a.ws_o[(base + p) * Dv + d], o);
-    for (int s = 0; s < a.num_splits; ++s) {
-      const int64_t pi = base + a.part_base + s;
-      const float w = exp2f(a.ws_lse[pi] - M);
-      if (w > 0.f) o = fmaf(w, a.ws_o[pi * Dv + d], o);
+  float M = kNegBig, L = 0.f;
+  f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < total; p0 += 8) {
+    float pl[8];
+    f32x4 po[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = p0 + j;
+      const int64_t pi = base + (idx < ns ? idx : a.part_base + idx - ns);
+      const bool ok = idx < total;
+      pl[j] = ok ? a.ws_lse[pi] : -INFINITY;
+      po[j] = ok ? *reinterpret_cast<const f32x4 *>(a.ws_o + pi * Dv + d) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    store_out<T>(a.out, (static_cast<int64_t>(b) * a.Hq + head) * Dv + d, o * inv);
+    float mx = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, pl[j]);
+    const float alpha = exp2f(M - mx);
+    L *= alpha;
+    O *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = exp2f(pl[j] - mx);
+      L += wj;
+      const f32x4 c = wj > 0.f ? po[j] * wj : f32x4{0.f, 0.f, 0.f, 0.f};
+      O += c;
+    }
+    M = mx;
   }
-  if (a.lse && threadIdx.x == 0) a.lse[static_cast<int64_t>(b) * a.Hq + head] = (M + log2f(L)) * kLn2;
+  const float inv = 1.f / L;
+  store_out4<T>(a.out, (static_cast<int64_t>(b) * a.Hq + head) * Dv + d, O * inv);
+  if (a.lse && d == 0) a.lse[static_cast<int64_t>(b) * a.Hq + head] = (M + log2f(L)) * kLn2;
 }
 
 }  // namespace
@@ -1005,41 +1132,39 @@ static hipError_t valu_g(int G, int mode, const AttnArgs &a, unsigned items, uns
 }
 
 template <int G>
-static hipError_t launch_tail(int mode, const AttnArgs &a, unsigned items, unsigned splits,
-                              hipStream_t stream) {
+static hipError_t launch_tail(const AttnArgs &a, unsigned items, unsigned splits, hipStream_t stream) {
   const uint64_t waves = static_cast<uint64_t>(items) * splits * a.Hkv;
   if (waves > 0x7fffffffull) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
   const int n = static_cast<int>(items), ns = static_cast<int>(splits);
-  if (mode == 0) launch(tail_bf16_kernel<G, 0>, grid, block, 0, stream, a, n, ns);
-  else launch(tail_bf16_kernel<G, 3>, grid, block, 0, stream, a, n, ns);
+  launch(tail_bf16_kernel<G>, grid, block, 0, stream, a, n, ns);
   return hipGetLastError();
+}
+
+hipError_t decode_tail_bf16(int G, const AttnArgs &a, unsigned batch, unsigned splits, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  switch (G) {
+    case 1: return launch_tail<1>(a, batch, splits, s);
+    case 2: return launch_tail<2>(a, batch, splits, s);
+    case 4: return launch_tail<4>(a, batch, splits, s);
+    case 8: return launch_tail<8>(a, batch, splits, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, unsigned splits,
                 hipStream_t s) {
   if (items == 0) return hipSuccess;
-  if (bf16 && (mode == 0 || mode == 3)) {
-    switch (G) {
-      case 1: return launch_tail<1>(mode, a, items, splits, s);
-      case 2: return launch_tail<2>(mode, a, items, splits, s);
-      case 4: return launch_tail<4>(mode, a, items, splits, s);
-      case 8: return launch_tail<8>(mode, a, items, splits, s);
-    }
-    return hipErrorInvalidValue;
-  }
   return bf16 ? valu_g<uint16_t, 128>(G, mode, a, items, splits, s)
               : valu_g<float, 64>(G, mode, a, items, splits, s);
 }
 
 template <int G>
-static hipError_t launch_mfma(bool seg, const AttnArgs &a, unsigned tiles, unsigned items,
-                              hipStream_t s) {
+static hipError_t launch_mfma(const AttnArgs &a, unsigned tiles, unsigned items, hipStream_t s) {
   const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
   if (n > 0x7fffffffull) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(256);
-  if (seg) launch(attn_mfma_kernel<G, true>, grid, block, 0, s, a, tiles, items);
-  else launch(attn_mfma_kernel<G, false>, grid, block, 0, s, a, tiles, items);
+  launch(attn_mfma_kernel<G>, grid, block, 0, s, a, tiles, items);
   return hipGetLastError();
 }
 
@@ -1066,23 +1191,25 @@ hipError_t decode_fused(int G, const AttnArgs &a, int max_rows, unsigned seg_ite
   return hipErrorInvalidValue;
 }
 
-hipError_t mfma(int G, bool seg, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
+hipError_t mfma(int G, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
   if (items == 0 || max_rows <= 0) return hipSuccess;
   const unsigned tiles = static_cast<unsigned>((max_rows + MF_BM - 1) / MF_BM);
   switch (G) {
-    case 1: return launch_mfma<1>(seg, a, tiles, items, s);
-    case 2: return launch_mfma<2>(seg, a, tiles, items, s);
-    case 4: return launch_mfma<4>(seg, a, tiles, items, s);
-    case 8: return launch_mfma<8>(seg, a, tiles, items, s);
+    case 1: return launch_mfma<1>(a, tiles, items, s);
+    case 2: return launch_mfma<2>(a, tiles, items, s);
+    case 4: return launch_mfma<4>(a, tiles, items, s);
+    case 8: return launch_mfma<8>(a, tiles, items, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t combine(bool bf16, const AttnArgs &a, int batch, int Dv, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  dim3 grid(batch, a.Hq), block(128);
-  if (bf16) launch(combine_kernel<uint16_t>, grid, block, 0, s, a, Dv);
-  else launch(combine_kernel<float>, grid, block, 0, s, a, Dv);
+  const uint64_t waves = static_cast<uint64_t>(batch) * ((a.Hq * Dv + 255) / 256);
+  if (waves > 0x7fffffffull) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+  if (bf16) launch(combine_kernel<uint16_t>, grid, block, 0, s, a, Dv, batch);
+  else launch(combine_kernel<float>, grid, block, 0, s, a, Dv, batch);
   return hipGetLastError();
 }
 

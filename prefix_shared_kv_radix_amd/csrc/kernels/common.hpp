@@ -56,4 +56,68 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Partial results merged by another block (possibly on another XCD, whose L2 is not
+// kept coherent with this one): written and read with device-scope relaxed atomic
+// accesses, which the compiler emits as sc1 loads/stores (served past the XCD's L2)
+// without any whole-cache writeback or invalidate.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_dev(float *p, f32x4 v) {
+  uint64_t *q = reinterpret_cast<uint64_t *>(p);
+  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 ld_dev(const float *p) {
+  const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+  const f32x2 a = __builtin_bit_cast(
+      f32x2, __hip_atomic_load(const_cast<uint64_t *>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const f32x2 b = __builtin_bit_cast(
+      f32x2, __hip_atomic_load(const_cast<uint64_t *>(q + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return f32x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ void st_dev1(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev1(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this wave's stores are complete (device-visible for sc1 stores), so an
+// atomic issued afterwards is ordered after them. A workgroup-scope fence does not wait
+// for stores on this target, and an agent-scope one would also write back the L2.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Arrival counter of a merge: returns the count before this arrival (relaxed, device scope).
+__device__ __forceinline__ int arrive(int32_t *c) {
+  return __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(int32_t *c) {
+  __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Eight transposed LDS reads (ds_read_b64_tr_b16) and the wait for them, as one block:
+// the results are valid when it returns. Written as assembly because the compiler orders
+// its own form of this read behind every outstanding global->LDS load (vmcnt(0)), which
+// would wait for the next tile's prefetch in the middle of the current one.
+__device__ __forceinline__ void lds_tr16_x8(u32x2 (&r)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 }  // namespace radix_dev

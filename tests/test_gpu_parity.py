@@ -113,6 +113,36 @@ def test_few_shot_bf16_small(use_plan, splits):
     _run(w, Checker(w), use_plan=use_plan, num_splits=splits)
 
 
+@pytest.mark.parametrize("use_plan,splits", [(True, 0), (False, 1), (False, 3)])
+def test_few_shot_bf16_host_slots(use_plan, splits):
+    """New decode slots read by the kernel from pinned host memory (no copy launch)."""
+    w = few_shot(12, gqa128_shape(), 200, 20, 29, 6, q_rows=4096)
+    _run(w, Checker(w), use_plan=use_plan, num_splits=splits, host_slots=True)
+
+
+def test_decode_rejects_pageable_new_slots():
+    """A pageable host slot list is refused on the host (E_INVAL) before any launch. The
+    call also has no workspace for its 3 key splits, so nothing could be launched even if
+    the pointer check were missing: the error text tells which check answered."""
+    import torch
+    from prefix_shared_kv_radix_amd import _lib
+    from prefix_shared_kv_radix_amd.runner import DeviceState
+    w = few_shot(12, gqa128_shape(), 40, 2, 8, 1, q_rows=64)
+    d = DeviceState(w, "cuda", 2, 64)
+    s = w.shape
+    B = 2
+    q = torch.zeros((B, s.num_q_heads, s.head_dim_qk), dtype=torch.bfloat16, device="cuda")
+    kv_new = torch.zeros((B, s.num_kv_heads, s.head_dim_qk), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, s.num_q_heads, s.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    seq = d.i32([5, 5])
+    pageable = torch.zeros(B, dtype=torch.int32)
+    assert not pageable.is_pinned()
+    with pytest.raises(_lib.RadixError, match="new_slots"):
+        _lib.attn_decode(d.shape, d.kv, q, kv_new, kv_new, None, pageable, d.rtt, None, seq, B, 8,
+                         None, 3, out, None, None)
+    torch.cuda.synchronize()
+
+
 def test_agent_two_level_segments_bf16():
     """Roots, branches and forks: decode reads two nested shared segments per request."""
     w = agent_branch(4, gqa128_shape(), 3, 200, 4, 70, 3, 6, q_rows=4096)
