@@ -740,8 +740,11 @@ constexpr int MF_BN = 64;    // keys per tile
 constexpr int MF_TILE = MF_BN * MF_D * 2;   // bytes of one K (or V) tile: 64 rows x 256 B
 
 // Byte offset of 16-byte chunk c of row r in a 64 x 256-byte tile. Chunks are XOR-swizzled
-// within 128-byte halves so rows read at the same column hit different LDS banks.
-__device__ __forceinline__ int mf_swz(int r, int c) { return r * 256 + ((c ^ (r & 7)) << 4); }
+// by a 4-bit function of the row so that, with 64 four-byte banks, the K operand reads
+// (16 lanes = 16 consecutive rows per b128 pass) and the V transpose reads (32 lanes
+// over 4 rows x 8 chunks per b64 pass) each touch every bank at most once.
+__device__ __forceinline__ int mf_row_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int mf_swz(int r, int c) { return r * 256 + ((c ^ mf_row_swz(r)) << 4); }
 
 
 __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
@@ -830,7 +833,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
 
   // loaders: wave w fills rows 16w .. 16w+15 of each tile, 4 rows per instruction;
   // lane i lands at byte 16*i of the instruction's 1 KB, i.e. row +i/16, physical chunk
-  // i%16, so it fetches logical chunk (i%16) ^ (row & 7) of that row.
+  // i%16, so it fetches logical chunk (i%16) ^ mf_row_swz(row) of that row.
   const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * MF_D * 2;
   const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * MF_D * 2;
   const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * MF_D * 2;
@@ -844,7 +847,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wave * 16 + 4 * j + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 7);
+      const int c = (lane & 15) ^ mf_row_swz(r);
       const int64_t off = static_cast<int64_t>(sl[j]) * row_bytes + c * 16;
       lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
       lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
