@@ -156,7 +156,7 @@ struct Timed {
 
 // Launch-shape tuning (overridable at build time).
 #ifndef RADIX_SEG_BLOCKS
-#define RADIX_SEG_BLOCKS 256
+#define RADIX_SEG_BLOCKS 128
 #endif
 #ifndef RADIX_TAIL_CHUNK
 #define RADIX_TAIL_CHUNK 512
@@ -165,8 +165,12 @@ struct Timed {
 #define RADIX_TAIL_WAVES 2048
 #endif
 
-// Key splits per shared segment: enough blocks to fill the chip (~512 for the MFMA
-// segment kernel), at least 256 keys per split, at most 16 splits.
+// Key splits per shared segment. The segment tiles of a decode step are latency-bound
+// (a handful of dependent loads, then one 64-key step after another) and share the
+// chip with the memory-bound tail waves, each holding a wave slot per SIMD while it
+// lives; so they get only ~128 blocks' worth of splits (at least 256 keys per split,
+// at most 16), which keeps them within the tail's run time while leaving the tail most
+// of the slots.
 int seg_splits_for(const radix_attn_shape *s, const radix_decode_plan *plan) {
   if (!plan || plan->num_segments <= 0) return 1;
   const bool mla = s->v_is_k_prefix != 0;

@@ -686,8 +686,21 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     *reinterpret_cast<u32x4 *>(vd + 16) = ldg16(vnew + 16);
   }
 
+  // A single private chunk whose shared-segment partials are all written already (the
+  // segment tiles run ahead of the tail waves) merges them straight into its output:
+  // no partial of its own, no arrival. The counter then holds exactly ns_b arrivals and
+  // no producer of this request is left, so the wave resets it.
+  int32_t *cnt = a.merge_cnt + static_cast<int64_t>(b) * a.Hkv + kvh;
+  bool fold = false;
+  if (nsplit == 1 && ns_b > 0) {
+    int seen = 0;
+    if (lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    fold = __builtin_amdgcn_readfirstlane(seen) == ns_b;
+    if (fold && lane == 0) reset_counter(cnt);
+  }
+
   // group r8 writes (head, half) pairs r8, r8 + 8, ...: 8 dims each
-  const bool direct = expected == 1;
+  const bool direct = expected == 1 || fold;
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -695,10 +708,36 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
       if (((2 * h + half) & 7) != r8) continue;
       const int head = kvh * G + h;
       const int d0 = sub * 16 + half * 8;
-      const float M = m[h], L = l[h];
+      float M = m[h], L = l[h];
       float O[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) O[e] = acc[h][half * 8 + e];
+      if (fold) {   // shared partials: o normalised, lse in log2 units
+        const int64_t hp = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
+        for (int p0 = 0; p0 < ns_b; p0 += 4) {
+          float pl[4];
+          f32x4 po[4][2];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = p0 + j < ns_b;
+            pl[j] = ok ? ld_dev1(a.ws_lse + hp + p0 + j) : -INFINITY;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              po[j][c] = ok ? ld_dev(a.ws_o + (hp + p0 + j) * D + d0 + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float mn = fmaxf(M, pl[j]);
+            const float wa = __builtin_amdgcn_exp2f(M - mn), wb = __builtin_amdgcn_exp2f(pl[j] - mn);
+            L = L * wa + wb;
+            M = mn;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) O[4 * c + e] = O[4 * c + e] * wa + po[j][c][e] * wb;
+          }
+        }
+      }
       const bool empty = !(L > 0.f);
       const float inv = empty ? 0.f : 1.f / L;
       const float lse2 = empty ? -INFINITY : M + log2f(L);
@@ -718,7 +757,6 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   if (direct) return;
   // arrive; the last producer merges (uniform branch: one counter per wave)
   wait_stores();
-  int32_t *cnt = a.merge_cnt + static_cast<int64_t>(b) * a.Hkv + kvh;
   int before = 0;
   if (lane == 0) before = arrive(cnt);
   before = __builtin_amdgcn_readfirstlane(before);
@@ -913,7 +951,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
         st[mb][i] = p;
         rs += p;
       }
-    l_run += rs + xor32(rs);
+    l_run += rs;   // this half's keys; the halves are added once, after the loop
 
     bf16x8 pb[2][2];
 #pragma unroll
@@ -956,6 +994,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     __syncthreads();
   }
 
+  l_run += xor32(l_run);
   if (!SEG && !rvalid) return;
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
