@@ -40,12 +40,6 @@ __device__ __forceinline__ float xor32f(float x) {
                                                                  __builtin_bit_cast(int, x)));
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_tr16(const uint8_t *p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) s16x4 *>(reinterpret_cast<uintptr_t>(p)));
-  return __builtin_bit_cast(u32x2, v);
-}
 __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void *>(
                                           reinterpret_cast<uintptr_t>(lds_base)),
@@ -131,10 +125,10 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
         const int c = fsub + 16 * i;
         if (c < 72) {
           const uint32_t x = raw[i][0], y = raw[i][1];
-          const u32x4 w = u32x4{pack_bf16x2(fp8_to_f32<0>(x) * rscale, fp8_to_f32<1>(x) * rscale),
-                                pack_bf16x2(fp8_to_f32<2>(x) * rscale, fp8_to_f32<3>(x) * rscale),
-                                pack_bf16x2(fp8_to_f32<0>(y) * rscale, fp8_to_f32<1>(y) * rscale),
-                                pack_bf16x2(fp8_to_f32<2>(y) * rscale, fp8_to_f32<3>(y) * rscale)};
+          const u32x4 w = u32x4{cvt_bf16x2(fp8_to_f32<0>(x) * rscale, fp8_to_f32<1>(x) * rscale),
+                                cvt_bf16x2(fp8_to_f32<2>(x) * rscale, fp8_to_f32<3>(x) * rscale),
+                                cvt_bf16x2(fp8_to_f32<0>(y) * rscale, fp8_to_f32<1>(y) * rscale),
+                                cvt_bf16x2(fp8_to_f32<2>(y) * rscale, fp8_to_f32<3>(y) * rscale)};
           *reinterpret_cast<u32x4 *>(&smem[stage][c < 64 ? offA(frow, c) : offB(frow, c - 64)]) = w;
         }
       }
@@ -179,11 +173,12 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sc, 0, 0, 0);
       if (s % RADIX_MLA_FENCE == RADIX_MLA_FENCE - 1) __builtin_amdgcn_sched_barrier(0);
     }
-    // swap partial scores with the other half of the pair; both add own + other
+    // swap partial scores with the other half of the pair; both add own + other (the
+    // barrier orders LDS only: the next tile's loads stay in flight)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       xs[wave][q][lane] = f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 other = xs[wave ^ 4][q][lane];
@@ -191,20 +186,22 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
       for (int e = 0; e < 4; ++e) sc[4 * q + e] += other[e];
     }
 
-    float mx = kNegBig;
+    if (kt + kBN > hi) {   // (uniform) ragged last tile
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kt + 8 * (i >> 2) + 4 * h + (i & 3);
-      const float v = key < hi ? sc[i] * a.scale_log2 : -INFINITY;
-      sc[i] = v;
-      mx = fmaxf(mx, v);
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt + 8 * (i >> 2) + 4 * h + (i & 3);
+        sc[i] = key < hi ? sc[i] : -INFINITY;
+      }
     }
-    mx = fmaxf(mx, xor32f(mx));
+    // raw scores: the scale (> 0) is applied to the maximum and inside the exponent
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[i], sc[i + 1]));
+    mx = fmaxf(mx, xor32f(mx)) * a.scale_log2;
     // rescale the accumulators only when some head's maximum grew noticeably
-    const bool grow = mx > m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
       const float mn = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - mn);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < kHalfV / 32; ++d) o[d] *= alpha;
@@ -213,29 +210,37 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
     float rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = exp2f(sc[i] - m_run);
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], a.scale_log2, -m_run));
       sc[i] = p;
       rs += p;
     }
-    l_run += rs + xor32f(rs);
+    l_run += rs;   // this half's keys; the two halves are added after the loop
     bf16x8 pb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(sc[8 * j + 2 * e], sc[8 * j + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(sc[8 * j + 2 * e], sc[8 * j + 2 * e + 1]);
       pb[j] = __builtin_bit_cast(bf16x8, w);
     }
+    // V^T operands of one value-dim block (4 transposed reads) at a time
+    const uint32_t tb = lds_addr(T);
 #pragma unroll
     for (int d = 0; d < kHalfV / 32; ++d) {
       const int dv0 = kHalfV * HALF + d * 32 + 16 * (g & 1) + 4 * (s16 & 3);
       const int c = dv0 >> 3, hb = (dv0 >> 2) & 1;
+      uint32_t ad[4];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r0 = 16 * j + vrow;
-        const u32x2 lo2 = lds_tr16(T + offA(r0, c) + 8 * hb);
-        const u32x2 hi2 = lds_tr16(T + offA(r0 + 8, c) + 8 * hb);
-        const u32x4 w = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        ad[2 * j] = tb + offA(r0, c) + 8 * hb;
+        ad[2 * j + 1] = tb + offA(r0 + 8, c) + 8 * hb;
+      }
+      u32x2 rv[4];
+      lds_tr16_x4(rv, ad);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 w = u32x4{rv[2 * j][0], rv[2 * j][1], rv[2 * j + 1][0], rv[2 * j + 1][1]};
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[j], o[d],
                                                         0, 0, 0);
       }
@@ -250,6 +255,7 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
 
   // ---- partial (normalised o, lse in log2 units) or, for a single part, the output;
   // each wave of the pair writes its value dims, half 0 the lse
+  l_run += xor32f(l_run);
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse2 = empty ? -INFINITY : m_run + log2f(l_run);
@@ -261,8 +267,8 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
       for (int g4 = 0; g4 < 4; ++g4) {
         const int dv = d * 32 + 8 * g4 + 4 * h;
         *reinterpret_cast<u32x2 *>(op + dv) =
-            u32x2{pack_bf16x2(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv),
-                  pack_bf16x2(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv)};
+            u32x2{cvt_bf16x2(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv),
+                  cvt_bf16x2(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv)};
       }
     if (a.lse && h == 0 && HALF == 0) a.lse[static_cast<int64_t>(b) * kHeads + head] = lse2 * kLn2;
     return;

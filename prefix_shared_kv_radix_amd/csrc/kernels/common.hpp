@@ -30,6 +30,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Two floats -> packed bf16 pair (lo in the low half) with the hardware conversion.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // OCP E4M3FN byte -> float via the gfx950 hardware conversion (byte `sel` of w).
 template <int SEL>
 __device__ __forceinline__ float fp8_to_f32(uint32_t w) {
@@ -99,6 +106,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete, then
+// s_barrier. Unlike __syncthreads() it does not wait for outstanding global loads, so a
+// prefetch of the next tile stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Eight transposed LDS reads (ds_read_b64_tr_b16) and the wait for them, as one block:
 // the results are valid when it returns. Written as assembly because the compiler orders
 // its own form of this read behind every outstanding global->LDS load (vmcnt(0)), which
@@ -117,6 +133,19 @@ __device__ __forceinline__ void lds_tr16_x8(u32x2 (&r)[8], const uint32_t (&a)[8
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
         "=&v"(r[6]), "=&v"(r[7])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+// Four transposed LDS reads and the wait for them (as lds_tr16_x8, fewer registers).
+__device__ __forceinline__ void lds_tr16_x4(u32x2 (&r)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
       : "memory");
 }
 
