@@ -909,15 +909,34 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     const uint8_t *Kt = smem[stage][0];
     const uint8_t *Vt = smem[stage][1];
 
+    // S^T per 32-key block. The eight K operands of block 0 are read up front; each is
+    // refilled with block 1's operand right after the MFMA that used it, so the reads
+    // overlap the MFMAs instead of one LDS latency being exposed per MFMA.
     f32x16 st[2];
+    {
+      bf16x8 ka[MF_D / 16];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      st[mb] = f32x16{};
+      for (int s = 0; s < MF_D / 16; ++s)
+        ka[s] = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(n, 2 * s + h));
+      st[0] = f32x16{};
+      st[1] = f32x16{};
 #pragma unroll
       for (int s = 0; s < MF_D / 16; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(mb * 32 + n, 2 * s + h));
-        st[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], st[mb], 0, 0, 0);
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st[0], 0, 0, 0);
+        ka[s] = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(32 + n, 2 * s + h));
       }
+#pragma unroll
+      for (int s = 0; s < MF_D / 16; ++s)
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st[1], 0, 0, 0);
+      // keep that order through scheduling: 8 LDS reads, then (MFMA, LDS read) x 8,
+      // then 8 MFMAs (masks: 0x100 LDS read, 0x008 MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int s = 0; s < MF_D / 16; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     if (kt + MF_BN > hi || kt + MF_BN - 1 > wave_q0) {   // (wave-uniform) ragged or diagonal tile
 #pragma unroll
@@ -971,24 +990,31 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     const int vrow0 = 4 * (g >> 1) + (s16 >> 2);
     const uint32_t vbase = lds_addr(Vt);
 #pragma unroll
-    for (int dvb = 0; dvb < 4; ++dvb) {
-      const int dv0 = dvb * 32 + 16 * (g & 1) + 4 * (s16 & 3);
-      const int c = dv0 >> 3, half = (dv0 >> 2) & 1;
-      uint32_t ad[8];
+    for (int d2 = 0; d2 < 2; ++d2) {   // two 32-dim value blocks per batch of reads
+      uint32_t ad[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {   // q = 2 * mb + j: keys 16q .. 16q+15 of the tile
-        const int r0 = 16 * q + vrow0;
-        ad[2 * q] = vbase + mf_swz(r0, c) + 8 * half;
-        ad[2 * q + 1] = vbase + mf_swz(r0 + 8, c) + 8 * half;
-      }
-      u32x2 rv[8];
-      lds_tr16_x8(rv, ad);
+      for (int dd = 0; dd < 2; ++dd) {
+        const int dv0 = (2 * d2 + dd) * 32 + 16 * (g & 1) + 4 * (s16 & 3);
+        const int c = dv0 >> 3, half = (dv0 >> 2) & 1;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 w = u32x4{rv[2 * q][0], rv[2 * q][1], rv[2 * q + 1][0], rv[2 * q + 1][1]};
-        o[dvb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
-                                                         pb[q >> 1][q & 1], o[dvb], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {   // q = 2 * mb + j: keys 16q .. 16q+15 of the tile
+          const int r0 = 16 * q + vrow0;
+          ad[8 * dd + 2 * q] = vbase + mf_swz(r0, c) + 8 * half;
+          ad[8 * dd + 2 * q + 1] = vbase + mf_swz(r0 + 8, c) + 8 * half;
+        }
       }
+      u32x2 rv[16];
+      lds_tr16_x16(rv, ad);
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int dvb = 2 * d2 + dd;
+          const u32x4 w = u32x4{rv[8 * dd + 2 * q][0], rv[8 * dd + 2 * q][1],
+                                rv[8 * dd + 2 * q + 1][0], rv[8 * dd + 2 * q + 1][1]};
+          o[dvb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
+                                                           pb[q >> 1][q & 1], o[dvb], 0, 0, 0);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
