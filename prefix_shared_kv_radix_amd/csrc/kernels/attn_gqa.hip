@@ -804,7 +804,8 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
 template <int G, bool SEG>
 __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item, int kvh,
                                           uint8_t (*smem)[2][MF_TILE]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
 
   int lo, hi, mem_off = 0, nrows, P = 0, b = 0;
@@ -868,6 +869,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   // first query position among this wave's rows: tiles wholly at or before it need no
   // causal mask (wave-uniform)
   const int wave_q0 = SEG ? 0x7fffffff : P + (tile * MF_BM + wave * 32) / G;
+  const bool wave_active = tile * MF_BM + wave * 32 < nrows;   // wave-uniform
 
   // loaders: wave w fills rows 16w .. 16w+15 of each tile, 4 rows per instruction;
   // lane i lands at byte 16*i of the instruction's 1 KB, i.e. row +i/16, physical chunk
@@ -908,6 +910,13 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     }
     const uint8_t *Kt = smem[stage][0];
     const uint8_t *Vt = smem[stage][1];
+    // a wave whose 32 rows are all past the block's rows (small shared segments) only
+    // loads its share of each tile and keeps the barriers, leaving the SIMD to others
+    if (!wave_active) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      continue;
+    }
 
     // S^T per 32-key block. The eight K operands of block 0 are read up front; each is
     // refilled with block 1's operand right after the MFMA that used it, so the reads
