@@ -183,30 +183,45 @@ radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const 
  * §一, applied to the requests sharing a radix-tree path). The rest of each
  * request's keys (positions from req_private_start on) is private.
  *
- * nodes[batch]: each request's admission node (pinned). Outputs (host arrays,
- * capacities in brackets):
+ * nodes[batch]: each request's admission node (pinned). A segment longer than
+ * split_keys keys is cut into ceil(len / split_keys) key chunks (split_keys <= 0:
+ * one chunk per segment); every chunk is a separate unit of work with its own
+ * partial result per member, so a long shared prefix is spread over several
+ * blocks while a short one stays whole. Outputs (host arrays, capacities in
+ * brackets):
  *   seg_row[cap_seg]      a member (batch index) whose slot list holds the segment
  *   seg_start/seg_end     key positions [start, end) of the segment
  *   seg_member_off[cap_seg+1], seg_members[cap_mem], seg_member_slot[cap_mem]
  *                         CSR of members; seg_member_slot = the segment's rank
  *                         on that member's path (0 = nearest the root)
- *   req_num_shared[batch], req_private_start[batch]
+ *   seg_split_off[cap_seg+1]  prefix sums of the chunk counts: segment s has
+ *                         chunks seg_split_off[s] .. seg_split_off[s+1]-1
+ *   seg_member_part[cap_mem]  the member's partial index of the segment's chunk
+ *                         0 (chunk k: + k); a request's partials of all its
+ *                         segments are 0 .. req_num_parts-1, root-most first
+ *   req_num_shared[batch] segments on the request's path, req_num_parts[batch]
+ *                         their chunks, req_private_start[batch]
  *   req_order[batch]      batch indices, requests with the same root-most shared
  *                         segment consecutive (then those without one)
- *   *num_segments, *num_member_entries, *max_members, *max_shared
+ *   *num_segments, *num_member_entries, *max_members, *max_shared,
+ *   *num_seg_items (= seg_split_off[num_segments]), *max_parts (largest
+ *   req_num_parts), *max_seg_splits (most chunks of one segment)
  * RADIX_E_INVAL if a capacity is too small (the needed counts are still written
  * to *num_segments and *num_member_entries). cap_seg >= 2*batch and
  * cap_mem >= batch*max-path-segments always suffice.
  * ====================================================================== */
 radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *nodes,
-                                    int32_t batch, int32_t min_members, int32_t cap_seg,
-                                    int32_t cap_mem, int32_t *seg_row, int32_t *seg_start,
-                                    int32_t *seg_end, int32_t *seg_member_off,
-                                    int32_t *seg_members, int32_t *seg_member_slot,
-                                    int32_t *req_num_shared, int32_t *req_private_start,
+                                    int32_t batch, int32_t min_members, int32_t split_keys,
+                                    int32_t cap_seg, int32_t cap_mem, int32_t *seg_row,
+                                    int32_t *seg_start, int32_t *seg_end,
+                                    int32_t *seg_member_off, int32_t *seg_members,
+                                    int32_t *seg_member_slot, int32_t *seg_split_off,
+                                    int32_t *seg_member_part, int32_t *req_num_shared,
+                                    int32_t *req_num_parts, int32_t *req_private_start,
                                     int32_t *req_order, int32_t *num_segments,
                                     int32_t *num_member_entries, int32_t *max_members,
-                                    int32_t *max_shared);
+                                    int32_t *max_shared, int32_t *num_seg_items,
+                                    int32_t *max_parts, int32_t *max_seg_splits);
 
 /* ======================================================================
  * Device side (HIP, gfx950). All pointers below marked "dev" are device
@@ -238,13 +253,19 @@ typedef struct {
   const int32_t *seg_row, *seg_start, *seg_end; /* dev [num_segments] */
   const int32_t *seg_member_off;                /* dev [num_segments + 1] */
   const int32_t *seg_members, *seg_member_slot; /* dev [num_member_entries] */
+  const int32_t *seg_split_off;                 /* dev [num_segments + 1] */
+  const int32_t *seg_member_part;               /* dev [num_member_entries] */
   const int32_t *req_num_shared;                /* dev [batch] */
+  const int32_t *req_num_parts;                 /* dev [batch] */
   const int32_t *req_private_start;             /* dev [batch] */
   const int32_t *req_order;                     /* dev [batch] or NULL */
   int32_t max_members;                          /* host: largest member count */
   int32_t max_shared;                           /* host: largest req_num_shared */
   int32_t max_seg_len;                          /* host: longest segment in tokens */
   int32_t min_private_start;                    /* host: smallest req_private_start */
+  int32_t num_seg_items;                        /* host: total segment chunks */
+  int32_t max_parts;                            /* host: largest req_num_parts */
+  int32_t max_seg_splits;                       /* host: most chunks of one segment */
 } radix_decode_plan;
 
 /* Shapes compiled into this library (anything else: RADIX_E_UNSUPPORTED):
@@ -264,7 +285,7 @@ radix_status radix_kv_store(const radix_attn_shape *shape, const radix_kv_buffer
 
 /* Workspace bytes radix_attn_decode needs for `batch` requests of at most
  * `max_seq_len` tokens with `plan` (NULL = no shared segments; only its host
- * fields num_segments, max_members, max_shared and max_seg_len are read) and
+ * fields are read: num_segments, max_parts, min_private_start) and
  * `num_splits` private splits (0 = the count radix_attn_decode chooses itself).
  * 0 bytes means the call needs no workspace. */
 radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int32_t batch,
@@ -301,8 +322,9 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
  * device memory or pinned host memory mapped into the device (then no copy to the
  * device is needed; the host must not change it until the call's work has run);
  * any other pointer is E_INVAL.
- * With a plan, each shared segment's keys are read once for all its members and
- * keys from req_private_start[b] on are read per request; without a plan (NULL)
+ * With a plan, each key chunk of a shared segment is read once for all the
+ * segment's members (one partial result per member and chunk) and keys from
+ * req_private_start[b] on are read per request; without a plan (NULL)
  * every request reads all its keys. A request's private keys are cut into
  * `num_splits` equal chunks of a common length (0 = choose: one chunk when the
  * tails are short and the batch fills the GPU, else 512-key chunks); all partial
@@ -311,9 +333,11 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
  *   workspace dev, at least radix_attn_decode_workspace_size bytes. bf16 K/V: the
  *   partial results are merged inside the one decode launch by whichever block
  *   finishes a request last, counted in the workspace's first 256 KiB (int32 per
- *   request and KV head; batch * Hkv <= 65536, else E_INVAL); that region must be
- *   zero before the first call on a workspace (e.g. allocate it zeroed) and every
- *   call leaves it zero. A workspace serves one call at a time.
+ *   request and KV head; batch * Hkv <= 65024, else E_INVAL), whose last 2 KiB
+ *   hold the work queue of the private-tail kernel, so a bf16 decode always needs a
+ *   workspace; that region must be zero before the first call on a workspace (e.g.
+ *   allocate it zeroed) and every call leaves it zero. A workspace serves one call
+ *   at a time.
  *   max_seq_len: host bound on seq_lens (grid sizing). */
 radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buffers *kv,
                                const void *q, const void *k_new, const void *v_new,

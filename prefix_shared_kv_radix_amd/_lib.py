@@ -55,10 +55,17 @@ class KVBuffers(C.Structure):
 class DecodePlan(C.Structure):
     _fields_ = [("num_segments", C.c_int32), ("num_member_entries", C.c_int32),
                 ("seg_row", _vp), ("seg_start", _vp), ("seg_end", _vp), ("seg_member_off", _vp),
-                ("seg_members", _vp), ("seg_member_slot", _vp), ("req_num_shared", _vp),
+                ("seg_members", _vp), ("seg_member_slot", _vp), ("seg_split_off", _vp),
+                ("seg_member_part", _vp), ("req_num_shared", _vp), ("req_num_parts", _vp),
                 ("req_private_start", _vp), ("req_order", _vp), ("max_members", C.c_int32),
-                ("max_shared", C.c_int32),
-                ("max_seg_len", C.c_int32), ("min_private_start", C.c_int32)]
+                ("max_shared", C.c_int32), ("max_seg_len", C.c_int32),
+                ("min_private_start", C.c_int32), ("num_seg_items", C.c_int32),
+                ("max_parts", C.c_int32), ("max_seg_splits", C.c_int32)]
+
+# array fields of a plan, in DecodePlan order
+_PLAN_ARRAYS = ("seg_row", "seg_start", "seg_end", "seg_member_off", "seg_members",
+                "seg_member_slot", "seg_split_off", "seg_member_part", "req_num_shared",
+                "req_num_parts", "req_private_start", "req_order")
 
 
 _SIGS = {
@@ -92,8 +99,7 @@ _SIGS = {
     "radix_profile_read": (C.c_int, [_i32p, C.POINTER(C.c_float), C.c_int32, _i32p]),
     "radix_kernel_name": (C.c_char_p, [C.c_int32]),
     "radix_tree_decode_plan": (C.c_int, [_vp, _i64p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                         _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
-                                         _i32p, _i32p, _i32p, _i32p, _i32p]),
+                                         C.c_int32] + [_i32p] * 19),
     "radix_attn_supported": (C.c_int, [C.POINTER(AttnShape), C.c_int]),
     "radix_kv_store": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp, _vp, _vp,
                                  C.c_int64, _vp]),
@@ -311,21 +317,27 @@ class RadixTree:
                                              out.ctypes.data_as(_i64p)))
         return out[:n]
 
-    def decode_plan(self, nodes, min_members: int = 2):
-        """Shared-segment plan (host arrays) for requests admitted at `nodes`."""
+    def decode_plan(self, nodes, min_members: int = 2, split_keys: int = 0):
+        """Shared-segment plan (host arrays) for requests admitted at `nodes`; segments
+        longer than split_keys keys are cut into chunks (0: one chunk per segment)."""
         nodes = np.ascontiguousarray(nodes, dtype=np.int64)
         B = len(nodes)
         cap_seg = max(2 * B, 1)
         cap_mem = max(B * 8, 1)
         while True:
-            seg = [np.zeros(cap_seg + (1 if k == 3 else 0), np.int32) for k in range(4)]
-            mem = [np.zeros(cap_mem, np.int32) for _ in range(2)]
-            req = [np.zeros(max(B, 1), np.int32) for _ in range(3)]
-            cnt = [C.c_int32() for _ in range(4)]
+            # seg_row, seg_start, seg_end [cap_seg]; seg_member_off, seg_split_off [cap_seg+1]
+            seg = [np.zeros(cap_seg + (1 if k >= 3 else 0), np.int32) for k in range(5)]
+            # seg_members, seg_member_slot, seg_member_part [cap_mem]
+            mem = [np.zeros(cap_mem, np.int32) for _ in range(3)]
+            # req_num_shared, req_num_parts, req_private_start, req_order [batch]
+            req = [np.zeros(max(B, 1), np.int32) for _ in range(4)]
+            cnt = [C.c_int32() for _ in range(7)]
+            p = lambda x: x.ctypes.data_as(_i32p)
             st = load().radix_tree_decode_plan(
-                self.h, nodes.ctypes.data_as(_i64p), B, int(min_members), cap_seg, cap_mem,
-                *[x.ctypes.data_as(_i32p) for x in seg], *[x.ctypes.data_as(_i32p) for x in mem],
-                *[x.ctypes.data_as(_i32p) for x in req], *[C.byref(c) for c in cnt])
+                self.h, nodes.ctypes.data_as(_i64p), B, int(min_members), int(split_keys),
+                cap_seg, cap_mem, p(seg[0]), p(seg[1]), p(seg[2]), p(seg[3]), p(mem[0]),
+                p(mem[1]), p(seg[4]), p(mem[2]), p(req[0]), p(req[1]), p(req[2]), p(req[3]),
+                *[C.byref(c) for c in cnt])
             ns, nm = cnt[0].value, cnt[1].value
             if st == E_INVAL and (ns > cap_seg or nm > cap_mem):
                 cap_seg, cap_mem = max(cap_seg, ns), max(cap_mem, nm)
@@ -335,8 +347,13 @@ class RadixTree:
         return HostPlan(seg_row=seg[0][:ns], seg_start=seg[1][:ns], seg_end=seg[2][:ns],
                         seg_member_off=seg[3][:ns + 1] if ns else np.zeros(1, np.int32),
                         seg_members=mem[0][:nm], seg_member_slot=mem[1][:nm],
-                        req_num_shared=req[0][:B], req_private_start=req[1][:B],
-                        req_order=req[2][:B], max_members=cnt[2].value, max_shared=cnt[3].value)
+                        seg_split_off=seg[4][:ns + 1] if ns else np.zeros(1, np.int32),
+                        seg_member_part=mem[2][:nm],
+                        req_num_shared=req[0][:B], req_num_parts=req[1][:B],
+                        req_private_start=req[2][:B], req_order=req[3][:B],
+                        max_members=cnt[2].value, max_shared=cnt[3].value,
+                        num_seg_items=cnt[4].value, max_parts=cnt[5].value,
+                        max_seg_splits=cnt[6].value)
 
 
 @dataclass
@@ -347,11 +364,17 @@ class HostPlan:
     seg_member_off: np.ndarray
     seg_members: np.ndarray
     seg_member_slot: np.ndarray
+    seg_split_off: np.ndarray
+    seg_member_part: np.ndarray
     req_num_shared: np.ndarray
+    req_num_parts: np.ndarray
     req_private_start: np.ndarray
     req_order: np.ndarray
     max_members: int
     max_shared: int
+    num_seg_items: int
+    max_parts: int
+    max_seg_splits: int
 
     @property
     def num_segments(self):
@@ -401,9 +424,10 @@ def host_plan_struct(plan):
     """DecodePlan carrying only the host scalars of a HostPlan (for workspace queries)."""
     if plan is None or plan.num_segments == 0:
         return None
-    return DecodePlan(plan.num_segments, len(plan.seg_members), None, None, None, None, None, None,
-                      None, None, None, plan.max_members, plan.max_shared, plan.max_seg_len,
-                      plan.min_private_start)
+    return DecodePlan(plan.num_segments, len(plan.seg_members), *([None] * len(_PLAN_ARRAYS)),
+                      plan.max_members, plan.max_shared, plan.max_seg_len,
+                      plan.min_private_start, plan.num_seg_items, plan.max_parts,
+                      plan.max_seg_splits)
 
 
 def decode_workspace_size(shape, batch, max_seq_len, plan, num_splits) -> int:
@@ -432,11 +456,10 @@ def device_plan(plan: HostPlan, device):
     import torch
     if plan is None or plan.num_segments == 0:
         return None, []
-    ts = [torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in
-          (plan.seg_row, plan.seg_start, plan.seg_end, plan.seg_member_off, plan.seg_members,
-           plan.seg_member_slot, plan.req_num_shared, plan.req_private_start, plan.req_order)]
+    ts = [torch.from_numpy(np.ascontiguousarray(getattr(plan, f))).to(device) for f in _PLAN_ARRAYS]
     dp = DecodePlan(plan.num_segments, len(plan.seg_members), *[_vp(t.data_ptr()) for t in ts],
-                    plan.max_members, plan.max_shared, plan.max_seg_len, plan.min_private_start)
+                    plan.max_members, plan.max_shared, plan.max_seg_len, plan.min_private_start,
+                    plan.num_seg_items, plan.max_parts, plan.max_seg_splits)
     return dp, ts
 
 

@@ -544,20 +544,29 @@ radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const 
 }
 
 radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *nodes,
-                                    int32_t batch, int32_t min_members, int32_t cap_seg,
-                                    int32_t cap_mem, int32_t *seg_row, int32_t *seg_start,
-                                    int32_t *seg_end, int32_t *seg_member_off,
-                                    int32_t *seg_members, int32_t *seg_member_slot,
-                                    int32_t *req_num_shared, int32_t *req_private_start,
+                                    int32_t batch, int32_t min_members, int32_t split_keys,
+                                    int32_t cap_seg, int32_t cap_mem, int32_t *seg_row,
+                                    int32_t *seg_start, int32_t *seg_end,
+                                    int32_t *seg_member_off, int32_t *seg_members,
+                                    int32_t *seg_member_slot, int32_t *seg_split_off,
+                                    int32_t *seg_member_part, int32_t *req_num_shared,
+                                    int32_t *req_num_parts, int32_t *req_private_start,
                                     int32_t *req_order, int32_t *num_segments,
                                     int32_t *num_member_entries, int32_t *max_members,
-                                    int32_t *max_shared) {
+                                    int32_t *max_shared, int32_t *num_seg_items,
+                                    int32_t *max_parts, int32_t *max_seg_splits) {
   RADIX_REQUIRE(tree && batch >= 0 && (batch == 0 || nodes) && min_members >= 2,
                 "bad arguments");
-  RADIX_REQUIRE(num_segments && num_member_entries && max_members && max_shared,
+  RADIX_REQUIRE(num_segments && num_member_entries && max_members && max_shared &&
+                    num_seg_items && max_parts && max_seg_splits,
                 "null output pointer");
-  RADIX_REQUIRE(batch == 0 || (req_num_shared && req_private_start && req_order),
+  RADIX_REQUIRE(batch == 0 || (req_num_shared && req_num_parts && req_private_start && req_order),
                 "null output pointer");
+  // key chunks of a segment of len tokens
+  auto chunks_of = [split_keys](int64_t len) -> int32_t {
+    if (split_keys <= 0 || len <= split_keys) return 1;
+    return static_cast<int32_t>((len + split_keys - 1) / split_keys);
+  };
   const RadixTree &t = tree->t;
   // paths (root first) and the number of running requests on each node
   std::vector<std::vector<int32_t>> paths(static_cast<size_t>(batch));
@@ -573,16 +582,19 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
   }
   // a segment = a maximal chain of path nodes with the same (>= min_members) count;
   // member sets nest along a path, so equal counts mean equal member sets
+  struct Member {
+    int32_t b, rank, part;
+  };
   struct Seg {
-    int32_t row, start, end;
-    std::vector<std::pair<int32_t, int32_t>> members;
+    int32_t row, start, end, chunks;
+    std::vector<Member> members;
   };
   std::vector<Seg> segs;
   std::unordered_map<int32_t, int32_t> seg_of_head;
-  int32_t total_mem = 0, maxsh = 0;
+  int32_t total_mem = 0, maxsh = 0, maxparts = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const auto &p = paths[b];
-    int32_t rank = 0;
+    int32_t rank = 0, parts = 0;
     int64_t start = 0, priv = 0;
     size_t i = 0;
     while (i < p.size() && count[p[i]] >= min_members) {
@@ -596,11 +608,13 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
       if (it == seg_of_head.end()) {
         sid = static_cast<int32_t>(segs.size());
         seg_of_head[head] = sid;
-        segs.push_back(Seg{b, static_cast<int32_t>(start), static_cast<int32_t>(end), {}});
+        segs.push_back(Seg{b, static_cast<int32_t>(start), static_cast<int32_t>(end),
+                           chunks_of(end - start), {}});
       } else {
         sid = it->second;
       }
-      segs[sid].members.emplace_back(b, rank);
+      segs[sid].members.push_back(Member{b, rank, parts});
+      parts += segs[sid].chunks;
       ++rank;
       ++total_mem;
       start = end;
@@ -608,8 +622,10 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
       i = j + 1;
     }
     req_num_shared[b] = rank;
+    req_num_parts[b] = parts;
     req_private_start[b] = static_cast<int32_t>(priv);
     maxsh = std::max(maxsh, rank);
+    maxparts = std::max(maxparts, parts);
   }
   // requests grouped by their root-most shared segment (segment creation order), then
   // the requests without any, in batch order
@@ -618,9 +634,9 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
     std::vector<uint8_t> placed(static_cast<size_t>(batch), 0);
     for (const auto &sg : segs)
       for (const auto &m : sg.members)
-        if (m.second == 0 && !placed[m.first]) {
-          placed[m.first] = 1;
-          req_order[k++] = m.first;
+        if (m.rank == 0 && !placed[m.b]) {
+          placed[m.b] = 1;
+          req_order[k++] = m.b;
         }
     for (int32_t b = 0; b < batch; ++b)
       if (!placed[b]) req_order[k++] = b;
@@ -628,27 +644,39 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
   *num_segments = static_cast<int32_t>(segs.size());
   *num_member_entries = total_mem;
   *max_shared = maxsh;
-  int32_t maxm = 0;
-  for (const auto &s : segs) maxm = std::max(maxm, static_cast<int32_t>(s.members.size()));
+  *max_parts = maxparts;
+  int32_t maxm = 0, items = 0, maxchunks = 0;
+  for (const auto &s : segs) {
+    maxm = std::max(maxm, static_cast<int32_t>(s.members.size()));
+    items += s.chunks;
+    maxchunks = std::max(maxchunks, s.chunks);
+  }
   *max_members = maxm;
+  *num_seg_items = items;
+  *max_seg_splits = maxchunks;
   RADIX_REQUIRE(static_cast<int32_t>(segs.size()) <= cap_seg && total_mem <= cap_mem,
                 "decode plan capacity too small");
   RADIX_REQUIRE(segs.empty() || (seg_row && seg_start && seg_end && seg_member_off &&
-                                 seg_members && seg_member_slot),
+                                 seg_members && seg_member_slot && seg_split_off &&
+                                 seg_member_part),
                 "null output pointer");
-  int32_t off = 0;
+  int32_t off = 0, chunk_off = 0;
   for (size_t s = 0; s < segs.size(); ++s) {
     seg_row[s] = segs[s].row;
     seg_start[s] = segs[s].start;
     seg_end[s] = segs[s].end;
     seg_member_off[s] = off;
+    seg_split_off[s] = chunk_off;
+    chunk_off += segs[s].chunks;
     for (auto &m : segs[s].members) {
-      seg_members[off] = m.first;
-      seg_member_slot[off] = m.second;
+      seg_members[off] = m.b;
+      seg_member_slot[off] = m.rank;
+      seg_member_part[off] = m.part;
       ++off;
     }
   }
   if (seg_member_off) seg_member_off[segs.size()] = off;
+  if (seg_split_off) seg_split_off[segs.size()] = chunk_off;
   return RADIX_OK;
 }
 

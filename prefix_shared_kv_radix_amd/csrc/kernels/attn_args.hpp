@@ -55,11 +55,13 @@ struct AttnArgs {
   const int32_t *prefix_lens, *extend_lens, *cu_extend;     // extend
   int batch;
   const int32_t *seg_row, *seg_start, *seg_end, *seg_member_off, *seg_members, *seg_member_slot;
+  // key chunks of segment s: seg_split_off[s] .. seg_split_off[s+1]-1; a member's partial
+  // of chunk k of its segment is seg_member_part[entry] + k
+  const int32_t *seg_split_off, *seg_member_part;
   int num_segments;
-  const int32_t *req_num_shared;
+  const int32_t *req_num_parts;   // segment partials of each request (NULL: none)
   int num_splits;   // private splits per request
   int split_chunk;  // keys per private split (all requests), when num_splits > 1
-  int seg_splits;   // key splits per shared segment
   int parts, part_base;  // partial slots per (request, head); private ones start at part_base
   // decode: the new token's K/V (read directly for the last position and stored by the
   // tail kernel) and its slot (appended to the slot list); all NULL when already stored
@@ -71,6 +73,8 @@ struct AttnArgs {
   float *ws_o, *ws_lse;
   // bf16 decode: arrival counters [batch, Hkv] of the in-kernel merge (zero between calls)
   int32_t *merge_cnt;
+  // bf16 private-tail kernel: work queue {next ticket, finished waves} (zero between calls)
+  int32_t *tail_queue;
   int Hq, Hkv;
   float scale_log2;
 };

@@ -94,7 +94,6 @@ AttnArgs attn_args(const radix_attn_shape *s, const radix_kv_buffers *kv, const 
   a.Hkv = s->num_kv_heads;
   a.scale_log2 = s->sm_scale * kLog2e;
   a.num_splits = 1;
-  a.seg_splits = 1;
   return a;
 }
 
@@ -155,36 +154,12 @@ struct Timed {
 };
 
 // Launch-shape tuning (overridable at build time).
-#ifndef RADIX_SEG_BLOCKS
-#define RADIX_SEG_BLOCKS 128
-#endif
 #ifndef RADIX_TAIL_CHUNK
 #define RADIX_TAIL_CHUNK 512
 #endif
 #ifndef RADIX_TAIL_WAVES
 #define RADIX_TAIL_WAVES 2048
 #endif
-
-// Key splits per shared segment. The segment tiles of a decode step are latency-bound
-// (a handful of dependent loads, then one 64-key step after another) and share the
-// chip with the memory-bound tail waves, each holding a wave slot per SIMD while it
-// lives; so they get only ~128 blocks' worth of splits (at least 256 keys per split,
-// at most 16), which keeps them within the tail's run time while leaving the tail most
-// of the slots.
-int seg_splits_for(const radix_attn_shape *s, const radix_decode_plan *plan) {
-  if (!plan || plan->num_segments <= 0) return 1;
-  const bool mla = s->v_is_k_prefix != 0;
-  const int G = s->num_q_heads / s->num_kv_heads;
-  const long rows = static_cast<long>(plan->max_members) * (mla ? 1 : G);
-  const long tiles = mla ? rows : (rows + 127) / 128;
-  const long blocks = tiles * plan->num_segments * s->num_kv_heads;
-  const long target = mla ? 1024 : RADIX_SEG_BLOCKS;   // the segment tiles overlap the tail waves
-  long ss = (target + blocks - 1) / (blocks > 0 ? blocks : 1);
-  const long cap = plan->max_seg_len / 256 > 1 ? plan->max_seg_len / 256 : 1;
-  if (ss > cap) ss = cap;
-  if (ss > 16) ss = 16;
-  return ss < 1 ? 1 : static_cast<int>(ss);
-}
 
 // Private-tail chunking: one chunk per request when the tails are short and the batch
 // alone gives ~2048 waves; otherwise 512-key chunks (more for very long tails), so
@@ -224,11 +199,15 @@ bool device_readable(const void *p) {
   return at.type == hipMemoryTypeHost && at.devicePointer == p;
 }
 
-// bf16 decode workspace: arrival counters of the in-kernel merge at a fixed place (the
-// first 256 KiB, one int32 per (request, KV head)), so a workspace reused by calls of
-// other shapes never finds partial data where counters are expected; partials follow.
-constexpr int64_t kMergeCounters = 1 << 16;
-constexpr size_t kMergeCounterBytes = kMergeCounters * sizeof(int32_t);
+// bf16 decode workspace: counters at a fixed place (the first 256 KiB), so a workspace
+// reused by calls of other shapes never finds partial data where counters are expected:
+// the in-kernel merge's arrival counters (one int32 per (request, KV head)), then the
+// private-tail kernel's work queue (16 counters, 128 bytes apart) in the last 2 KiB;
+// partials follow.
+constexpr int64_t kCounterInts = 1 << 16;
+constexpr size_t kMergeCounterBytes = kCounterInts * sizeof(int32_t);
+constexpr int64_t kQueueInts = 512;
+constexpr int64_t kMergeCounters = kCounterInts - kQueueInts;
 
 // partial outputs [batch, Hq, parts, Dv] and their lse [batch, Hq, parts], fp32, rounded
 // up to 256 bytes
@@ -292,17 +271,16 @@ radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int
   if (num_splits == 0)
     num_splits = auto_splits(batch, shape->num_kv_heads, private_len_bound(max_seq_len, plan));
   const bool use_plan = plan && plan->num_segments > 0;
-  const size_t shared = use_plan ? static_cast<size_t>(plan->max_shared) *
-                                       static_cast<size_t>(seg_splits_for(shape, plan))
-                                 : 0;
+  const size_t shared = use_plan ? static_cast<size_t>(plan->max_parts) : 0;
   const size_t parts = shared + static_cast<size_t>(num_splits);
+  const bool bf16 = shape->q_dtype == RADIX_BF16;
   if (!use_plan && num_splits == 1) {
-    *bytes = 0;  // single pass, nothing to merge
+    // single pass, nothing to merge (bf16: the counter region still holds the work queue)
+    *bytes = bf16 ? kMergeCounterBytes : 0;
     return RADIX_OK;
   }
-  // bf16: the in-kernel merge's arrival counters occupy a fixed region in front
-  *bytes = (shape->q_dtype == RADIX_BF16 ? kMergeCounterBytes : 0) +
-           partials_bytes(shape, batch, parts);
+  // bf16: the counters occupy a fixed region in front
+  *bytes = (bf16 ? kMergeCounterBytes : 0) + partials_bytes(shape, batch, parts);
   return RADIX_OK;
 }
 
@@ -373,9 +351,12 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   const bool use_plan = plan && plan->num_segments > 0;
   if (use_plan) {
     REQUIRE(plan->seg_row && plan->seg_start && plan->seg_end && plan->seg_member_off &&
-                plan->seg_members && plan->seg_member_slot && plan->req_num_shared &&
+                plan->seg_members && plan->seg_member_slot && plan->seg_split_off &&
+                plan->seg_member_part && plan->req_num_shared && plan->req_num_parts &&
                 plan->req_private_start && plan->num_member_entries > 0 &&
-                plan->max_members > 0 && plan->max_shared > 0,
+                plan->max_members > 0 && plan->max_shared > 0 &&
+                plan->num_seg_items >= plan->num_segments && plan->max_parts >= plan->max_shared &&
+                plan->max_seg_splits > 0,
             "incomplete decode plan");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -437,16 +418,16 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   const int splits = num_splits > 0 ? num_splits
                                     : auto_splits(batch, shape->num_kv_heads,
                                                   private_len_bound(max_seq_len, plan));
-  const int seg_splits = use_plan ? seg_splits_for(shape, plan) : 1;
-  const int max_shared = use_plan ? plan->max_shared * seg_splits : 0;
+  const int max_shared = use_plan ? plan->max_parts : 0;   // segment partials per request
   const int parts = max_shared + splits;
   const bool direct = !use_plan && splits == 1;
   size_t need = 0;
   radix_attn_decode_workspace_size(shape, batch, max_seq_len, plan, splits, &need);
-  REQUIRE(direct || (workspace && workspace_bytes >= need), "decode workspace too small");
+  REQUIRE((direct && kind != Kind::GqaBf16) || (workspace && workspace_bytes >= need),
+          "decode workspace too small");
   REQUIRE(direct || kind != Kind::GqaBf16 ||
               static_cast<int64_t>(batch) * shape->num_kv_heads <= kMergeCounters,
-          "batch * num_kv_heads above the merge counter capacity (65536)");
+          "batch * num_kv_heads above the merge counter capacity (65024)");
   char *ws_parts = static_cast<char *>(workspace) + (kind == Kind::GqaBf16 ? kMergeCounterBytes : 0);
   float *ws_o = direct ? nullptr : reinterpret_cast<float *>(ws_parts);
   float *ws_lse = direct ? nullptr
@@ -460,7 +441,6 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     const int plen = private_len_bound(max_seq_len, use_plan ? plan : nullptr);
     a.split_chunk = ((plen + splits - 1) / splits + 15) & ~15;
   }
-  a.seg_splits = seg_splits;
   a.parts = parts;
   a.part_base = max_shared;
   a.ws_o = ws_o;
@@ -478,18 +458,21 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     a.seg_member_off = plan->seg_member_off;
     a.seg_members = plan->seg_members;
     a.seg_member_slot = plan->seg_member_slot;
+    a.seg_split_off = plan->seg_split_off;
+    a.seg_member_part = plan->seg_member_part;
     a.num_segments = plan->num_segments;
-    a.req_num_shared = plan->req_num_shared;
+    a.req_num_parts = plan->req_num_parts;
     a.private_start = plan->req_private_start;
   }
   if (bf16) {
     // one launch per step: partials are merged in-kernel by their last producer
     a.merge_cnt = direct ? nullptr : static_cast<int32_t *>(workspace);
+    a.tail_queue = static_cast<int32_t *>(workspace) + kMergeCounters;
     Timed t(use_plan ? K_DECODE_FUSED : K_DECODE_TAIL, s);
     if (use_plan)
       return hip_status(radix_launch::decode_fused(
                             G, a, plan->max_members * G,
-                            static_cast<unsigned>(plan->num_segments * seg_splits),
+                            static_cast<unsigned>(plan->num_seg_items),
                             static_cast<unsigned>(batch), static_cast<unsigned>(splits), s),
                         "decode launch");
     return hip_status(radix_launch::decode_tail_bf16(G, a, static_cast<unsigned>(batch),
@@ -498,7 +481,8 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   }
   if (use_plan) {
     Timed t(K_SEGMENT_VALU, s);
-    st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries, seg_splits, s),
+    st = hip_status(radix_launch::valu(false, G, 2, a, plan->num_member_entries,
+                                                       plan->max_seg_splits, s),
                     "segment launch");
     if (st != RADIX_OK) return st;
   }

@@ -24,6 +24,8 @@
 //                     members of a shared radix segment x heads (decode: one
 //                     read of the segment's KV serves every member).
 //   combine_kernel    merges per-request partial results.
+#include <atomic>
+
 #include "common.hpp"
 #include "attn_args.hpp"
 #include "radix_attn.h"
@@ -153,6 +155,7 @@ __device__ __forceinline__ void valu_body(const AttnArgs &a, int w, int n_items,
   const int item = w / (a.Hkv * nsplit);
 
   int b, lo, hi, part = 0;
+  int pieces = nsplit;   // key chunks of this item's range
   int64_t q_row;
   const int32_t *rtt_row;
   if (MODE == 1) {
@@ -170,17 +173,21 @@ __device__ __forceinline__ void valu_body(const AttnArgs &a, int w, int n_items,
     rtt_row = rtt_row_of(a, b);
     part = a.part_base + split;
   } else {
+    // item = member entry; split = key chunk of its segment (nsplit = most chunks of a
+    // segment: the waves past this segment's own count have no work)
     const int sg = find_owner(a.seg_member_off, a.num_segments, item);
+    pieces = a.seg_split_off[sg + 1] - a.seg_split_off[sg];
+    if (split >= pieces) return;
     b = a.seg_members[item];
     lo = a.seg_start[sg];
     hi = a.seg_end[sg];
     q_row = b;
     rtt_row = rtt_row_of(a, a.seg_row[sg]);
-    part = a.seg_member_slot[item] * a.seg_splits + split;
+    part = a.seg_member_part[item] + split;
   }
   // TAIL: common chunk length (a.split_chunk) so uneven requests spread evenly;
-  // MODE 2: the segment's own length cut into nsplit pieces
-  const int chunk = (TAIL && nsplit > 1) ? a.split_chunk : ((hi - lo + nsplit - 1) / nsplit + 15) & ~15;
+  // MODE 2: the segment's own length cut into its chunk count
+  const int chunk = (TAIL && nsplit > 1) ? a.split_chunk : ((hi - lo + pieces - 1) / pieces + 15) & ~15;
   const int s_lo = lo + split * chunk;
   const int s_hi = min(hi, s_lo + chunk);
 
@@ -330,7 +337,7 @@ __device__ __forceinline__ void valu_body(const AttnArgs &a, int w, int n_items,
   }
 
   // lane group g writes heads g, g+4, ...; dims sub*EPL .. sub*EPL+EPL-1
-  const int nshared = (MODE == 3 && a.req_num_shared) ? a.req_num_shared[b] * a.seg_splits : 0;
+  const int nshared = (MODE == 3 && a.req_num_parts) ? a.req_num_parts[b] : 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if ((h & 3) != grp) continue;
@@ -425,60 +432,81 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-// Merges every partial of request b for the G query heads of KV head kvh into the
-// bf16 output (and lse): lane -> 8 dims of one head, 512 values per pass. Partials of
-// shared segments come first ([0, req_num_shared[b] * seg_splits)), then the private
-// chunks ([part_base, part_base + num_splits)); an empty partial has lse -inf and
-// weight 0. Called by the last producer to arrive, after its counter read.
-template <int G>
-__device__ __forceinline__ void merge_request_bf16(const AttnArgs &a, int b, int kvh) {
+// Merges every partial of up to NR requests (bs[0 .. n-1], wave-uniform, n >= 1; nparts[r]
+// = request bs[r]'s segment-chunk partial count) for the G query heads of KV head kvh
+// into the bf16 output (and lse): lane -> 8 dims of one head, 512 values per pass.
+// Partials of shared-segment chunks come first ([0, nparts)), then the private chunks
+// ([part_base, part_base + num_splits)); an empty partial has lse -inf and weight 0.
+// The first four partials of all NR requests are loaded before any is folded, so the
+// merges take one memory round trip rather than one per request. Called by the last
+// producer to arrive, after its counter read.
+template <int G, int NR>
+__device__ __forceinline__ void merge_requests_bf16(const AttnArgs &a, const int (&bs)[NR],
+                                                    const int (&nparts)[NR], int n, int kvh) {
   const int lane = threadIdx.x & 63;
-  const int ns = a.req_num_shared ? a.req_num_shared[b] * a.seg_splits : 0;
-  const int total = ns + a.num_splits;
 #pragma unroll
   for (int c = 0; c < (G * 128 + 511) / 512; ++c) {
     const int e = c * 512 + lane * 8;
     if (e >= G * 128) break;
     const int head = kvh * G + e / 128, d = e % 128;
-    const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
-    float M = kNegBig, L = 0.f;
-    f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = O0;
-    for (int p0 = 0; p0 < total; p0 += 4) {
-      float pl[4];
-      f32x4 pa[4], pb[4];
+    float pl[NR][4];
+    f32x4 pa[NR][4], pb[NR][4];
+    // partials p0 .. p0+3 of request slot r (slots past n repeat request 0; indices past
+    // the request's count re-read its partial 0 with weight 0): loads never branch
+    auto load4 = [&](int r, int p0) {
+      const int b = r < n ? bs[r] : bs[0];
+      const int ns = r < n ? nparts[r] : nparts[0];
+      const int total = ns + a.num_splits;
+      const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int idx = p0 + j;
+        const int idx = p0 + j < total ? p0 + j : 0;
         const int64_t pi = base + (idx < ns ? idx : a.part_base + idx - ns);
-        const bool ok = idx < total;
-        pl[j] = ok ? ld_dev1(a.ws_lse + pi) : -INFINITY;
-        pa[j] = ok ? ld_dev(a.ws_o + pi * 128 + d) : f32x4{0.f, 0.f, 0.f, 0.f};
-        pb[j] = ok ? ld_dev(a.ws_o + pi * 128 + d + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const float l = ld_dev1(a.ws_lse + pi);
+        pl[r][j] = p0 + j < total ? l : -INFINITY;
+        pa[r][j] = ld_dev(a.ws_o + pi * 128 + d);
+        pb[r][j] = ld_dev(a.ws_o + pi * 128 + d + 4);
       }
+    };
+    auto fold4 = [&](int r, float &M, float &L, f32x4 &O0, f32x4 &O1) {
       float mx = M;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, pl[j]);
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, pl[r][j]);
       const float alpha = exp2f(M - mx);
       L *= alpha;
       O0 *= alpha;
       O1 *= alpha;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float wj = exp2f(pl[j] - mx);
+        const float wj = exp2f(pl[r][j] - mx);
         L += wj;
         if (wj > 0.f) {
-          O0 += pa[j] * wj;
-          O1 += pb[j] * wj;
+          O0 += pa[r][j] * wj;
+          O1 += pb[r][j] * wj;
         }
       }
       M = mx;
+    };
+#pragma unroll
+    for (int r = 0; r < NR; ++r) load4(r, 0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (r >= n) break;
+      const int b = bs[r];
+      float M = kNegBig, L = 0.f;
+      f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = O0;
+      fold4(r, M, L, O0, O1);
+      for (int p0 = 4; p0 < nparts[r] + a.num_splits; p0 += 4) {   // more than 4 partials
+        load4(r, p0);
+        fold4(r, M, L, O0, O1);
+      }
+      const float inv = 1.f / L;
+      uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + (static_cast<int64_t>(b) * a.Hq + head) * 128 + d;
+      *reinterpret_cast<u32x4 *>(op) =
+          u32x4{pack2bf(O0[0] * inv, O0[1] * inv), pack2bf(O0[2] * inv, O0[3] * inv),
+                pack2bf(O1[0] * inv, O1[1] * inv), pack2bf(O1[2] * inv, O1[3] * inv)};
+      if (a.lse && d == 0) a.lse[static_cast<int64_t>(b) * a.Hq + head] = (M + log2f(L)) * kLn2;
     }
-    const float inv = 1.f / L;
-    uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + (static_cast<int64_t>(b) * a.Hq + head) * 128 + d;
-    *reinterpret_cast<u32x4 *>(op) =
-        u32x4{pack2bf(O0[0] * inv, O0[1] * inv), pack2bf(O0[2] * inv, O0[3] * inv),
-              pack2bf(O1[0] * inv, O1[1] * inv), pack2bf(O1[2] * inv, O1[3] * inv)};
-    if (a.lse && d == 0) a.lse[static_cast<int64_t>(b) * a.Hq + head] = (M + log2f(L)) * kLn2;
   }
 }
 
@@ -486,12 +514,22 @@ __device__ __forceinline__ void merge_request_bf16(const AttnArgs &a, int b, int
 #define RADIX_TAIL_STAGES 3
 #endif
 
+__device__ __forceinline__ int32_t take_ticket(int32_t *q);
+
+// One private-tail item w = (request, split, KV head) on one wave. With a work queue
+// (queue != NULL) the wave draws its next ticket into `ticket` (lane 0) once its keys
+// are read, so the atomic's latency overlaps the rest of the item.
 template <int G>
-__device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_items, int nsplit) {
+__device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_items, int nsplit,
+                                               int32_t *queue = nullptr, int32_t *ticket = nullptr) {
   constexpr int D = 128;
   constexpr int NB = RADIX_TAIL_STAGES;
   constexpr float kGrow = 8.f;
-  const int lane = threadIdx.x & 63, r8 = lane >> 3, sub = lane & 7;
+  int lane = threadIdx.x & 63;
+  // opaque per call, so that the values derived from the lane index are computed for each
+  // item instead of being kept live across the work-queue loop (register pressure)
+  asm volatile("" : "+v"(lane));
+  const int r8 = lane >> 3, sub = lane & 7;
   w = __builtin_amdgcn_readfirstlane(w);   // one work item per wave: its indices are scalar
   if (w >= n_items * nsplit * a.Hkv) return;
   const int kvh = w % a.Hkv;
@@ -522,7 +560,7 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     vnew = reinterpret_cast<const char *>(a.v_new) + off;
     if (store_new) new_slot = a.new_slots ? a.new_slots[b] : a.rtt[new_at];
   }
-  const int ns_b = a.req_num_shared ? a.req_num_shared[b] * a.seg_splits : 0;
+  const int ns_b = a.req_num_parts ? a.req_num_parts[b] : 0;
   const int expected = ns_b + nsplit;   // producers of this request's output
 
   // q: G heads x this lane's 16 dims, packed bf16 pairs (unscaled)
@@ -661,6 +699,8 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     compute(r8 == 0, false, kr, vr);
   }
 
+  if (queue) *ticket = take_ticket(queue);
+
   // merge the 8 row groups (lanes l, l^8, l^16, l^32 hold the same dims)
 #pragma unroll
   for (int mask = 8; mask <= 32; mask <<= 1) {
@@ -762,13 +802,57 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   before = __builtin_amdgcn_readfirstlane(before);
   if (before == expected - 1) {
     if (lane == 0) reset_counter(cnt);
-    merge_request_bf16<G>(a, b, kvh);
+    const int bs[1] = {b}, nps[1] = {ns_b};
+    merge_requests_bf16<G, 1>(a, bs, nps, 1, kvh);
   }
 }
 
+// Private-tail decode as a work queue: the grid holds only as many blocks as fit on the
+// GPU at once. Wave i first takes item i (request, split, KV head); when there are more
+// items than waves, it then takes further items by ticket until it draws one past the
+// end. Items differ widely in length (empty, partial and full chunks); launched as one
+// block per four items, the hardware's in-order block dispatch leaves CUs idle behind
+// long-running blocks, which the queue avoids.
+// The queue has kTailShards counters, 128 bytes apart (atomics on one address are
+// serialised, and thousands of waves draw at about the same time): wave i draws from
+// shard k = i % S (S = kTailShards, or nwaves if smaller), whose ticket t names item
+// nwaves + k + t * S.
+// Every wave of shard k draws exactly one ticket past the shard's last item and stops,
+// so the shard's counter ends at exactly (its items) + (its waves): the wave that draws
+// the final value is the last to touch that counter and resets it for the next call.
+constexpr int kTailShards = 16;
+constexpr int kTailShardStride = 32;   // int32 elements between shard counters
+
+__device__ __forceinline__ int32_t take_ticket(int32_t *q) {
+  int32_t t = 0;
+  if ((threadIdx.x & 63) == 0)
+    t = __hip_atomic_fetch_add(q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return t;   // lane 0's value; read with readfirstlane where it is used
+}
+
 template <int G>
-__global__ __launch_bounds__(256) void tail_bf16_kernel(AttnArgs a, int n_items, int nsplit) {
-  tail_bf16_body<G>(a, blockIdx.x * 4 + (threadIdx.x >> 6), n_items, nsplit);
+__global__ __launch_bounds__(256, G >= 8 ? 1 : 2) void tail_bf16_kernel(AttnArgs a, int n_items,
+                                                                        int nsplit) {
+  const int total = n_items * nsplit * a.Hkv;
+  const int nwaves = static_cast<int>(gridDim.x) * 4;
+  int w = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);
+  w = __builtin_amdgcn_readfirstlane(w);
+  const int shards = nwaves < kTailShards ? nwaves : kTailShards;   // each has >= 1 wave
+  const int k = w % shards;
+  int32_t *queue = total > nwaves ? a.tail_queue + k * kTailShardStride : nullptr;   // uniform
+  // final counter value of shard k: its items past the first round plus its waves
+  const int rest = total - nwaves - k;
+  const int last = (rest > 0 ? (rest + shards - 1) / shards : 0) +
+                   (nwaves - k + shards - 1) / shards - 1;
+  while (w < total) {
+    int32_t ticket = 0;
+    tail_bf16_body<G>(a, w, n_items, nsplit, queue, &ticket);
+    if (!queue) break;
+    const int t = __builtin_amdgcn_readfirstlane(ticket);
+    if (t == last && (threadIdx.x & 63) == 0)
+      __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w = nwaves + k + t * shards;
+  }
 }
 
 // ------------------------------------------------------------------ MFMA kernel
@@ -808,7 +892,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
 
-  int lo, hi, mem_off = 0, nrows, P = 0, b = 0;
+  int lo, hi, mem_off = 0, nrows, P = 0, b = 0, ks = 0;
   const int32_t *rtt_row;
   if (!SEG) {
     b = item;
@@ -821,13 +905,15 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     hi = P + i_last + 1;
     rtt_row = rtt_row_of(a, b);
   } else {
-    // blockIdx.y = segment * seg_splits + key split of that segment
-    const int sg = item / a.seg_splits, ks = item % a.seg_splits;
+    // item = key chunk: chunk ks of segment sg (the segment's own chunk count)
+    const int sg = find_owner(a.seg_split_off, a.num_segments, item);
+    ks = item - a.seg_split_off[sg];
+    const int pieces = a.seg_split_off[sg + 1] - a.seg_split_off[sg];
     mem_off = a.seg_member_off[sg];
     nrows = (a.seg_member_off[sg + 1] - mem_off) * G;
     if (tile * MF_BM >= nrows) return;
     const int s0 = a.seg_start[sg], s1 = a.seg_end[sg];
-    const int chunk = ((s1 - s0 + a.seg_splits - 1) / a.seg_splits + MF_BN - 1) / MF_BN * MF_BN;
+    const int chunk = ((s1 - s0 + pieces - 1) / pieces + MF_BN - 1) / MF_BN * MF_BN;
     lo = s0 + ks * chunk;
     hi = min(s1, lo + chunk);
     rtt_row = rtt_row_of(a, a.seg_row[sg]);
@@ -1050,9 +1136,13 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     // partial of this key range for every member row, then one arrival per member
     // request (its head-0 lane); a member whose other producers have all arrived is
     // merged here by the whole wave
+    // the lanes that arrive for a member request read its partial count now, so that
+    // load overlaps the partial stores
+    const bool arriver = rvalid && hg == 0 && h == 0;
+    const int np_q = arriver ? a.req_num_parts[q_tok] : 0;
     int last_b = -1;
     if (rvalid) {
-      const int part = a.seg_member_slot[mem_off + qi] * a.seg_splits + item % a.seg_splits;
+      const int part = a.seg_member_part[mem_off + qi] + ks;
       const int64_t pi = (q_tok * a.Hq + head) * a.parts + part;
       float *wp = a.ws_o + pi * MF_D;
 #pragma unroll
@@ -1066,20 +1156,34 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       if (h == 0) st_dev1(a.ws_lse + pi, lse2);
     }
     wait_stores();
-    if (rvalid && hg == 0 && h == 0) {
+    if (arriver) {
       const int bq = static_cast<int>(q_tok);
-      const int expected = a.req_num_shared[bq] * a.seg_splits + a.num_splits;
       int32_t *cnt = a.merge_cnt + static_cast<int64_t>(bq) * a.Hkv + kvh;
-      if (arrive(cnt) == expected - 1) {
+      if (arrive(cnt) == np_q + a.num_splits - 1) {
         reset_counter(cnt);
         last_b = bq;
       }
     }
+    // requests this wave completed, merged NR at a time (fewer for 8 heads per KV head,
+    // whose merge pass covers two 512-value halves)
+    constexpr int NR = G >= 8 ? 2 : 4;
     uint64_t pending = __builtin_amdgcn_ballot_w64(last_b >= 0);
     while (pending) {
-      const int l = __builtin_ctzll(pending);
-      pending &= pending - 1;
-      merge_request_bf16<G>(a, __builtin_amdgcn_readlane(last_b, l), kvh);
+      int bs[NR], nps[NR], n = 0;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (pending) {
+          const int l = __builtin_ctzll(pending);
+          pending &= pending - 1;
+          bs[r] = __builtin_amdgcn_readlane(last_b, l);
+          nps[r] = __builtin_amdgcn_readlane(np_q, l);
+          ++n;
+        } else {
+          bs[r] = bs[0];
+          nps[r] = nps[0];
+        }
+      }
+      merge_requests_bf16<G, NR>(a, bs, nps, n, kvh);
     }
   }
 }
@@ -1135,7 +1239,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int Dv, int ba
   const int e = (w % per_req) * 256 + lane * 4;
   if (e >= a.Hq * Dv) return;
   const int head = e / Dv, d = e % Dv;
-  const int ns = a.req_num_shared ? a.req_num_shared[b] * a.seg_splits : 0;
+  const int ns = a.req_num_parts ? a.req_num_parts[b] : 0;
   const int total = ns + a.num_splits;
   const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
   float M = kNegBig, L = 0.f;
@@ -1212,7 +1316,24 @@ template <int G>
 static hipError_t launch_tail(const AttnArgs &a, unsigned items, unsigned splits, hipStream_t stream) {
   const uint64_t waves = static_cast<uint64_t>(items) * splits * a.Hkv;
   if (waves > 0x7fffffffull) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+  if (!a.tail_queue) return hipErrorInvalidValue;
+  // blocks resident at once on this device (cached per device)
+  static std::atomic<int> resident[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int fit = dev < 64 ? resident[dev].load(std::memory_order_relaxed) : 0;
+  if (fit == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tail_bf16_kernel<G>, 256, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    fit = per_cu * cus > 0 ? per_cu * cus : 1;
+    if (dev < 64) resident[dev].store(fit, std::memory_order_relaxed);
+  }
+  const uint64_t blocks = (waves + 3) / 4;
+  dim3 grid(static_cast<unsigned>(blocks < static_cast<uint64_t>(fit) ? blocks : fit)), block(256);
   const int n = static_cast<int>(items), ns = static_cast<int>(splits);
   launch(tail_bf16_kernel<G>, grid, block, 0, stream, a, n, ns);
   return hipGetLastError();

@@ -54,6 +54,11 @@ class EpisodeLog:
 
 _TORCH_KV = {"f32": "float32", "bf16": "bfloat16", "fp8": "uint8"}
 
+# Shared segments longer than this many keys are cut into key chunks in the decode plan,
+# each its own unit of work (a 2048-token prefix: 2 chunks; a 4096-token one: 4), so a
+# long shared prefix is not one block's sequential walk while short ones stay whole.
+SEG_SPLIT_KEYS = 1024
+
 
 class DeviceState:
     """Device buffers for one workload: the K/V pool, slot lists, tables of inputs."""
@@ -102,7 +107,8 @@ class Engine:
 
     def __init__(self, workload, device=None, use_plan: bool = True, num_splits: int = 0,
                  on_extend: Optional[Callable] = None, on_decode: Optional[Callable] = None,
-                 min_members: int = 2, host_slots: bool = False):
+                 min_members: int = 2, host_slots: bool = False,
+                 split_keys: int = SEG_SPLIT_KEYS):
         self.w = workload
         self.pool = _lib.KVPool(workload.pool_slots)
         self.tree = _lib.RadixTree(self.pool)
@@ -112,6 +118,7 @@ class Engine:
         self.on_extend = on_extend
         self.on_decode = on_decode
         self.min_members = min_members
+        self.split_keys = split_keys
         self.host_slots = host_slots   # decode reads new slots from pinned host memory
         self._ws = None
         self.content = np.full(workload.pool_slots, -1, np.int64)   # harness bookkeeping
@@ -164,7 +171,8 @@ class Engine:
             self.dirty.extend(a.row[a.prefix_len:] for a in rnd.admissions)
         if ph.n_decode:
             if self.use_plan and B > 1:
-                rnd.plan = self.tree.decode_plan([a.node for a in rnd.admissions], self.min_members)
+                rnd.plan = self.tree.decode_plan([a.node for a in rnd.admissions], self.min_members,
+                                                 self.split_keys)
             for s in range(ph.n_decode):
                 slots = self.tree.alloc(B)
                 rnd.decode_slots[s] = slots

@@ -120,6 +120,23 @@ def test_few_shot_bf16_host_slots(use_plan, splits):
     _run(w, Checker(w), use_plan=use_plan, num_splits=splits, host_slots=True)
 
 
+@pytest.mark.parametrize("split_keys", [16, 24])
+def test_tiny_fp32_segment_chunks(split_keys):
+    """The 64-token shared prefix cut into key chunks by the plan: 4 full chunks, or 3
+    chunks of which the last is empty (chunk lengths round up to 16 keys)."""
+    w = config(1)
+    _run(w, Checker(w), split_keys=split_keys)
+
+
+@pytest.mark.parametrize("split_keys", [40, 100])
+def test_agent_segment_chunks_bf16(split_keys):
+    """Roots of 200 tokens and branches of 70 cut into key chunks (lengths round up to
+    64 keys, so split_keys 40 leaves an empty last root chunk); every chunk is its own
+    partial in the in-kernel merge."""
+    w = agent_branch(4, gqa128_shape(), 3, 200, 4, 70, 3, 6, q_rows=4096)
+    _run(w, Checker(w, extend_sample=4), split_keys=split_keys)
+
+
 def test_decode_rejects_pageable_new_slots():
     """A pageable host slot list is refused on the host (E_INVAL) before any launch. The
     call also has no workspace for its 3 key splits, so nothing could be launched even if

@@ -161,22 +161,27 @@ def test_decode_plan_matches_tree_structure():
                                       rows[0])
 
 
+def _random_admissions(seed):
+    """A small tree of cached prompts and a batch admitted on it (tree, pool, admissions)."""
+    rng = random.Random(seed)
+    p = _lib.KVPool(4000)
+    t = _lib.RadixTree(p)
+    base = [[rng.randint(0, 2) for _ in range(rng.randint(1, 6))] for _ in range(4)]
+    for s in base:
+        m, row, node = t.admit(s)
+        t.finish(s, row, m, node)
+    prompts = []
+    for _ in range(rng.randint(2, 10)):
+        b = rng.choice(base)
+        prompts.append(b[:rng.randint(0, len(b))] + [rng.randint(0, 2) for _ in range(rng.randint(0, 3))])
+    return t, p, [t.admit(pr) for pr in prompts]
+
+
 def test_decode_plan_brute_force():
     """Random batches: for each pair of requests, the shared segments they have in
     common cover exactly the prefix of identical slots up to the shallower private start."""
     for seed in range(20):
-        rng = random.Random(seed)
-        p = _lib.KVPool(4000)
-        t = _lib.RadixTree(p)
-        base = [[rng.randint(0, 2) for _ in range(rng.randint(1, 6))] for _ in range(4)]
-        for s in base:
-            m, row, node = t.admit(s)
-            t.finish(s, row, m, node)
-        prompts = []
-        for _ in range(rng.randint(2, 10)):
-            b = rng.choice(base)
-            prompts.append(b[:rng.randint(0, len(b))] + [rng.randint(0, 2) for _ in range(rng.randint(0, 3))])
-        adm = [t.admit(pr) for pr in prompts]
+        t, p, adm = _random_admissions(seed)
         plan = t.decode_plan([a[2] for a in adm])
         for i in range(len(adm)):
             segs = [s for s in range(plan.num_segments)
@@ -193,6 +198,46 @@ def test_decode_plan_brute_force():
                 for j in mem:
                     np.testing.assert_array_equal(adm[j][1][plan.seg_start[s]:plan.seg_end[s]],
                                                   adm[i][1][plan.seg_start[s]:plan.seg_end[s]])
+
+
+def test_decode_plan_key_chunks():
+    """Key chunks: the segments do not depend on split_keys; segment s gets
+    ceil(len / split_keys) chunks (1 when split_keys <= 0 or len <= split_keys); each
+    request's partial indices (segments in path order, a segment's chunks consecutive)
+    tile 0 .. req_num_parts-1 exactly; the host counts agree with the arrays."""
+    checked = 0
+    for seed in range(30):
+        t, p, adm = _random_admissions(seed)
+        nodes = [a[2] for a in adm]
+        ref = t.decode_plan(nodes)
+        for sk in (0, -3, 1, 2, 3, 5):
+            plan = t.decode_plan(nodes, 2, sk)
+            for f in ("seg_row", "seg_start", "seg_end", "seg_member_off", "seg_members",
+                      "seg_member_slot", "req_num_shared", "req_private_start", "req_order"):
+                np.testing.assert_array_equal(getattr(plan, f), getattr(ref, f))
+            lens = plan.seg_end - plan.seg_start
+            want = np.array([1 if sk <= 0 or n <= sk else -(-n // sk) for n in lens], np.int64)
+            assert plan.seg_split_off[0] == 0
+            np.testing.assert_array_equal(np.diff(plan.seg_split_off), want)
+            assert plan.num_seg_items == int(want.sum())
+            assert plan.max_seg_splits == (int(want.max()) if len(want) else 0)
+            for i in range(len(adm)):
+                owned = []   # (rank, first part, chunks) of request i's segments
+                for s_ in range(plan.num_segments):
+                    lo, hi = plan.seg_member_off[s_], plan.seg_member_off[s_ + 1]
+                    for e in range(lo, hi):
+                        if plan.seg_members[e] == i:
+                            owned.append((plan.seg_member_slot[e], plan.seg_member_part[e], want[s_]))
+                owned.sort()
+                assert [o[0] for o in owned] == list(range(len(owned)))
+                nxt = 0
+                for _, first, n in owned:
+                    assert first == nxt
+                    nxt += n
+                assert plan.req_num_parts[i] == nxt
+                checked += len(owned)
+            assert plan.max_parts == (int(plan.req_num_parts.max()) if len(adm) else 0)
+    assert checked > 50
 
 
 def test_library_exports_every_declared_symbol():
