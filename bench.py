@@ -9,8 +9,10 @@ free duplicates, unpin). Query/K/V inputs are staged in HBM before the timed
 region; slot lists are produced inside it by the host tree and copied over.
 
 Prints one JSON line. `value` = decode tokens generated per second of episode
-time (whole job); the breakdown, per-kernel event timings, the roofline of the
-dominant kernel and the CPU oracle's rate on a bounded sample are included.
+time (whole job); the breakdown, per-kernel event timings (taken over a second,
+identical run of the same steps, since an event pair around every launch slows the
+step), the roofline of the dominant kernel and the CPU oracle's rate on a bounded
+sample are included.
 """
 from __future__ import annotations
 
@@ -346,16 +348,25 @@ def main():
         ep.run()
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
-    _lib.profile_enable(1 << 17)
+    # timed region: K steps with only three events per round (the extend/decode split)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ep.run(mark=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    print(f"[bench] timed {args.steps} steps in {t1 - t0:.3f}s", file=sys.stderr, flush=True)
+    # the same K steps again with a HIP event pair around every launch (per-kernel
+    # durations for the roofline); kept out of the region above because the per-launch
+    # events cost the step several percent
+    _lib.profile_enable(1 << 17)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ep.run()
+    torch.cuda.synchronize()
     prof = _lib.profile_read(1 << 17)
     _lib.profile_enable(0)
-    print(f"[bench] timed {args.steps} steps in {t1 - t0:.3f}s", file=sys.stderr, flush=True)
+    print(f"[bench] kernel-timed {args.steps} more steps", file=sys.stderr, flush=True)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     dec_tokens = sum(st["B"] * st["ph"].n_decode for st in ep.staged)

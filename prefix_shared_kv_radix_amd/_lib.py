@@ -456,11 +456,22 @@ def device_plan(plan: HostPlan, device):
     import torch
     if plan is None or plan.num_segments == 0:
         return None, []
-    ts = [torch.from_numpy(np.ascontiguousarray(getattr(plan, f))).to(device) for f in _PLAN_ARRAYS]
-    dp = DecodePlan(plan.num_segments, len(plan.seg_members), *[_vp(t.data_ptr()) for t in ts],
+    # all arrays in one pinned buffer and one asynchronous copy: a copy from pageable
+    # memory would make the host wait for everything already queued on the stream
+    arrays = [np.ascontiguousarray(getattr(plan, f), dtype=np.int32) for f in _PLAN_ARRAYS]
+    offs = np.concatenate([[0], np.cumsum([len(x) for x in arrays])])
+    host = torch.empty(max(int(offs[-1]), 1), dtype=torch.int32, pin_memory=True)
+    hv = host.numpy()
+    for x, o in zip(arrays, offs[:-1]):
+        hv[o:o + len(x)] = x
+    dev = torch.empty_like(host, device=device)
+    dev.copy_(host, non_blocking=True)
+    base = dev.data_ptr()
+    dp = DecodePlan(plan.num_segments, len(plan.seg_members),
+                    *[_vp(base + 4 * int(o)) for o in offs[:-1]],
                     plan.max_members, plan.max_shared, plan.max_seg_len, plan.min_private_start,
                     plan.num_seg_items, plan.max_parts, plan.max_seg_splits)
-    return dp, ts
+    return dp, [dev, host]
 
 
 def attn_decode(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token, req_rows, seq_lens,
