@@ -327,7 +327,7 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
  * req_private_start[b] on are read per request; without a plan (NULL)
  * every request reads all its keys. A request's private keys are cut into
  * `num_splits` equal chunks of a common length (0 = choose: one chunk when the
- * tails are short and the batch fills the GPU, else 512-key chunks); all partial
+ * tails are short and the batch fills the GPU, else 768-key chunks); all partial
  * results are merged exactly by their log-sum-exp.
  *   q dev [batch, Hq, Dqk]; out dev [batch, Hq, Dv]; lse_out dev [batch, Hq] or NULL;
  *   workspace dev, at least radix_attn_decode_workspace_size bytes. bf16 K/V: the

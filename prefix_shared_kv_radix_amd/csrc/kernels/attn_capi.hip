@@ -155,18 +155,22 @@ struct Timed {
 
 // Launch-shape tuning (overridable at build time).
 #ifndef RADIX_TAIL_CHUNK
-#define RADIX_TAIL_CHUNK 512
+#define RADIX_TAIL_CHUNK 768
+#endif
+#ifndef RADIX_TAIL_UNSPLIT
+#define RADIX_TAIL_UNSPLIT 1024
 #endif
 #ifndef RADIX_TAIL_WAVES
 #define RADIX_TAIL_WAVES 2048
 #endif
 
-// Private-tail chunking: one chunk per request when the tails are short and the batch
-// alone gives ~2048 waves; otherwise 512-key chunks (more for very long tails), so
-// requests of very different lengths still spread evenly over the GPU.
+// Private-tail chunking: one chunk per request when the tails are short (<= 1024 keys)
+// and the batch alone gives ~2048 waves; otherwise 768-key chunks (more for very long
+// tails), which the work-queue kernel spreads evenly over the GPU whatever the mix of
+// request lengths.
 constexpr int kTailChunk = RADIX_TAIL_CHUNK;
 int auto_splits(int batch, int hkv, int private_len) {
-  if (private_len <= 2 * kTailChunk && batch * hkv >= RADIX_TAIL_WAVES) return 1;
+  if (private_len <= RADIX_TAIL_UNSPLIT && batch * hkv >= RADIX_TAIL_WAVES) return 1;
   int s = (private_len + kTailChunk - 1) / kTailChunk;
   if (s > 64) s = 64;
   return s < 1 ? 1 : s;
