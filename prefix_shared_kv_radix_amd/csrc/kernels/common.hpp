@@ -68,12 +68,15 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
 // accesses, which the compiler emits as sc1 loads/stores (served past the XCD's L2)
 // without any whole-cache writeback or invalidate.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+// One 16-byte store with the same cache policy (sc1) that a device-scope relaxed atomic
+// store gets: a pair of 8-byte atomic stores reached HBM as partial-line writes, about
+// twice the bytes. The compiler does not track this store, so its own waits can only
+// get stricter; callers wait for it with wait_stores() before publishing (arrive()).
+// A store of more than 8 bytes needs one wait state before a vector ALU instruction
+// may overwrite its data registers; the compiler adds it only for stores it emits
+// itself, so the block carries its own.
 __device__ __forceinline__ void st_dev(float *p, f32x4 v) {
-  uint64_t *q = reinterpret_cast<uint64_t *>(p);
-  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ f32x4 ld_dev(const float *p) {
   const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
