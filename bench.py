@@ -115,6 +115,7 @@ class Episode:
                 seq = st["prompt_len"][None, :] + 1 + np.arange(n)[:, None]
                 st["seq_dev"] = d.i32(seq)
                 st["seq_host"] = seq
+                st["seq_max"] = [int(x) for x in seq.max(axis=1)]
                 st["dout"] = torch.empty((B, s.num_q_heads, s.head_dim_v), dtype=d.q_dtype, device=dev)
                 st["slot_pin"] = torch.empty((2, n, B), dtype=torch.int32, pin_memory=True)
                 st["slot_dev"] = torch.empty((n, B), dtype=torch.int32, device=dev)
@@ -169,10 +170,14 @@ class Episode:
             n = ph.n_decode
             if n:
                 pin = st["slot_pin"][par]
+                pin_np = pin.numpy()              # the pinned rows, written in place
+                stream = torch.cuda.current_stream()
+                cols = st["prompt_len"]
+                ar = np.arange(B)
                 for s in range(n):
                     slots = tree.alloc(B)
-                    rows[np.arange(B), st["prompt_len"] + s] = slots
-                    pin[s].copy_(torch.from_numpy(slots))
+                    rows[ar, cols + s] = slots
+                    pin_np[s] = slots
                     # GQA decode reads the new slots from pinned host memory (no copy launch);
                     # the MLA path stores the new rows in a separate launch first, from device memory
                     slot_arg = pin[s]
@@ -182,8 +187,8 @@ class Episode:
                     _lib.attn_decode(d.shape, d.kv, st["dq"][s], st["dk"][s],
                                      None if st["dv"] is None else st["dv"][s],
                                      None if st["dsc"] is None else st["dsc"][s], slot_arg,
-                                     d.rtt, None, st["seq_dev"][s], B, int(st["seq_host"][s].max()),
-                                     plan_dev, self.splits, st["dout"], None, self.ws)
+                                     d.rtt, None, st["seq_dev"][s], B, st["seq_max"][s],
+                                     plan_dev, self.splits, st["dout"], None, self.ws, stream)
             if mark:
                 marks.append(("round_end", torch.cuda.Event(enable_timing=True)))
                 marks[-1][1].record()

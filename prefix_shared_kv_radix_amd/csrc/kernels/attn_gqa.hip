@@ -700,6 +700,24 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   }
 
   if (queue) *ticket = take_ticket(queue);
+  // the new token's row goes to its slot now (no wave reads it: the newest key is taken
+  // from k_new/v_new), so its loads and stores overlap the reduction below
+  if (store_new && r8 == 0) {
+    if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[new_at] = new_slot;
+    char *kd = const_cast<char *>(kb) + static_cast<int64_t>(new_slot) * row_bytes;
+    char *vd = const_cast<char *>(vb) + static_cast<int64_t>(new_slot) * row_bytes;
+    *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
+    *reinterpret_cast<u32x4 *>(kd + 16) = ldg16(knew + 16);
+    *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
+    *reinterpret_cast<u32x4 *>(vd + 16) = ldg16(vnew + 16);
+  }
+  // merge counter of this (request, KV head), read now for the single-chunk fold below
+  // so that its round trip overlaps the cross-lane reduction (a stale, lower count only
+  // means the ordinary path: own partial and arrival)
+  int32_t *cnt = a.merge_cnt + static_cast<int64_t>(b) * a.Hkv + kvh;
+  const bool may_fold = nsplit == 1 && ns_b > 0;
+  int seen = 0;
+  if (may_fold && lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // merge the 8 row groups (lanes l, l^8, l^16, l^32 hold the same dims)
 #pragma unroll
@@ -716,25 +734,12 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     }
   }
 
-  if (store_new && r8 == 0) {
-    if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[new_at] = new_slot;
-    char *kd = const_cast<char *>(kb) + static_cast<int64_t>(new_slot) * row_bytes;
-    char *vd = const_cast<char *>(vb) + static_cast<int64_t>(new_slot) * row_bytes;
-    *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
-    *reinterpret_cast<u32x4 *>(kd + 16) = ldg16(knew + 16);
-    *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
-    *reinterpret_cast<u32x4 *>(vd + 16) = ldg16(vnew + 16);
-  }
-
   // A single private chunk whose shared-segment partials are all written already (the
   // segment tiles run ahead of the tail waves) merges them straight into its output:
   // no partial of its own, no arrival. The counter then holds exactly ns_b arrivals and
   // no producer of this request is left, so the wave resets it.
-  int32_t *cnt = a.merge_cnt + static_cast<int64_t>(b) * a.Hkv + kvh;
   bool fold = false;
-  if (nsplit == 1 && ns_b > 0) {
-    int seen = 0;
-    if (lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (may_fold) {
     fold = __builtin_amdgcn_readfirstlane(seen) == ns_b;
     if (fold && lane == 0) reset_counter(cnt);
   }
