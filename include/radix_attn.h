@@ -199,6 +199,12 @@ radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const 
  *   seg_member_part[cap_mem]  the member's partial index of the segment's chunk
  *                         0 (chunk k: + k); a request's partials of all its
  *                         segments are 0 .. req_num_parts-1, root-most first
+ *   seg_items[cap_items*8]  one record per chunk i (i = seg_split_off[s] + k):
+ *                         {lo, hi, member offset, member count, row, s, k, 0};
+ *                         chunk k of segment s covers key positions [lo, hi) =
+ *                         [start + k*clen, min(end, start + (k+1)*clen)) with clen =
+ *                         ceil(len / chunks) rounded up to 64 (trailing chunks may be
+ *                         empty: lo = hi = end)
  *   req_num_shared[batch] segments on the request's path, req_num_parts[batch]
  *                         their chunks, req_private_start[batch]
  *   req_order[batch]      batch indices, requests with the same root-most shared
@@ -207,16 +213,17 @@ radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const 
  *   *num_seg_items (= seg_split_off[num_segments]), *max_parts (largest
  *   req_num_parts), *max_seg_splits (most chunks of one segment)
  * RADIX_E_INVAL if a capacity is too small (the needed counts are still written
- * to *num_segments and *num_member_entries). cap_seg >= 2*batch and
- * cap_mem >= batch*max-path-segments always suffice.
+ * to *num_segments, *num_member_entries and *num_seg_items). cap_seg >= 2*batch
+ * and cap_mem >= batch*max-path-segments always suffice.
  * ====================================================================== */
 radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *nodes,
                                     int32_t batch, int32_t min_members, int32_t split_keys,
-                                    int32_t cap_seg, int32_t cap_mem, int32_t *seg_row,
-                                    int32_t *seg_start, int32_t *seg_end,
+                                    int32_t cap_seg, int32_t cap_mem, int32_t cap_items,
+                                    int32_t *seg_row, int32_t *seg_start, int32_t *seg_end,
                                     int32_t *seg_member_off, int32_t *seg_members,
                                     int32_t *seg_member_slot, int32_t *seg_split_off,
-                                    int32_t *seg_member_part, int32_t *req_num_shared,
+                                    int32_t *seg_member_part, int32_t *seg_items,
+                                    int32_t *req_num_shared,
                                     int32_t *req_num_parts, int32_t *req_private_start,
                                     int32_t *req_order, int32_t *num_segments,
                                     int32_t *num_member_entries, int32_t *max_members,
@@ -255,6 +262,7 @@ typedef struct {
   const int32_t *seg_members, *seg_member_slot; /* dev [num_member_entries] */
   const int32_t *seg_split_off;                 /* dev [num_segments + 1] */
   const int32_t *seg_member_part;               /* dev [num_member_entries] */
+  const int32_t *seg_items;                     /* dev [num_seg_items * 8] chunk records */
   const int32_t *req_num_shared;                /* dev [batch] */
   const int32_t *req_num_parts;                 /* dev [batch] */
   const int32_t *req_private_start;             /* dev [batch] */

@@ -56,7 +56,8 @@ class DecodePlan(C.Structure):
     _fields_ = [("num_segments", C.c_int32), ("num_member_entries", C.c_int32),
                 ("seg_row", _vp), ("seg_start", _vp), ("seg_end", _vp), ("seg_member_off", _vp),
                 ("seg_members", _vp), ("seg_member_slot", _vp), ("seg_split_off", _vp),
-                ("seg_member_part", _vp), ("req_num_shared", _vp), ("req_num_parts", _vp),
+                ("seg_member_part", _vp), ("seg_items", _vp), ("req_num_shared", _vp),
+                ("req_num_parts", _vp),
                 ("req_private_start", _vp), ("req_order", _vp), ("max_members", C.c_int32),
                 ("max_shared", C.c_int32), ("max_seg_len", C.c_int32),
                 ("min_private_start", C.c_int32), ("num_seg_items", C.c_int32),
@@ -64,8 +65,8 @@ class DecodePlan(C.Structure):
 
 # array fields of a plan, in DecodePlan order
 _PLAN_ARRAYS = ("seg_row", "seg_start", "seg_end", "seg_member_off", "seg_members",
-                "seg_member_slot", "seg_split_off", "seg_member_part", "req_num_shared",
-                "req_num_parts", "req_private_start", "req_order")
+                "seg_member_slot", "seg_split_off", "seg_member_part", "seg_items",
+                "req_num_shared", "req_num_parts", "req_private_start", "req_order")
 
 
 _SIGS = {
@@ -99,7 +100,7 @@ _SIGS = {
     "radix_profile_read": (C.c_int, [_i32p, C.POINTER(C.c_float), C.c_int32, _i32p]),
     "radix_kernel_name": (C.c_char_p, [C.c_int32]),
     "radix_tree_decode_plan": (C.c_int, [_vp, _i64p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                         C.c_int32] + [_i32p] * 19),
+                                         C.c_int32, C.c_int32] + [_i32p] * 20),
     "radix_attn_supported": (C.c_int, [C.POINTER(AttnShape), C.c_int]),
     "radix_kv_store": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp, _vp, _vp,
                                  C.c_int64, _vp]),
@@ -324,23 +325,25 @@ class RadixTree:
         B = len(nodes)
         cap_seg = max(2 * B, 1)
         cap_mem = max(B * 8, 1)
+        cap_items = max(4 * B, 1)
         while True:
             # seg_row, seg_start, seg_end [cap_seg]; seg_member_off, seg_split_off [cap_seg+1]
             seg = [np.zeros(cap_seg + (1 if k >= 3 else 0), np.int32) for k in range(5)]
             # seg_members, seg_member_slot, seg_member_part [cap_mem]
             mem = [np.zeros(cap_mem, np.int32) for _ in range(3)]
+            items = np.zeros(cap_items * 8, np.int32)   # chunk records
             # req_num_shared, req_num_parts, req_private_start, req_order [batch]
             req = [np.zeros(max(B, 1), np.int32) for _ in range(4)]
             cnt = [C.c_int32() for _ in range(7)]
             p = lambda x: x.ctypes.data_as(_i32p)
             st = load().radix_tree_decode_plan(
                 self.h, nodes.ctypes.data_as(_i64p), B, int(min_members), int(split_keys),
-                cap_seg, cap_mem, p(seg[0]), p(seg[1]), p(seg[2]), p(seg[3]), p(mem[0]),
-                p(mem[1]), p(seg[4]), p(mem[2]), p(req[0]), p(req[1]), p(req[2]), p(req[3]),
-                *[C.byref(c) for c in cnt])
-            ns, nm = cnt[0].value, cnt[1].value
-            if st == E_INVAL and (ns > cap_seg or nm > cap_mem):
-                cap_seg, cap_mem = max(cap_seg, ns), max(cap_mem, nm)
+                cap_seg, cap_mem, cap_items, p(seg[0]), p(seg[1]), p(seg[2]), p(seg[3]),
+                p(mem[0]), p(mem[1]), p(seg[4]), p(mem[2]), p(items), p(req[0]), p(req[1]),
+                p(req[2]), p(req[3]), *[C.byref(c) for c in cnt])
+            ns, nm, ni = cnt[0].value, cnt[1].value, cnt[4].value
+            if st == E_INVAL and (ns > cap_seg or nm > cap_mem or ni > cap_items):
+                cap_seg, cap_mem, cap_items = max(cap_seg, ns), max(cap_mem, nm), max(cap_items, ni)
                 continue
             _check(st)
             break
@@ -348,7 +351,7 @@ class RadixTree:
                         seg_member_off=seg[3][:ns + 1] if ns else np.zeros(1, np.int32),
                         seg_members=mem[0][:nm], seg_member_slot=mem[1][:nm],
                         seg_split_off=seg[4][:ns + 1] if ns else np.zeros(1, np.int32),
-                        seg_member_part=mem[2][:nm],
+                        seg_member_part=mem[2][:nm], seg_items=items[:8 * ni],
                         req_num_shared=req[0][:B], req_num_parts=req[1][:B],
                         req_private_start=req[2][:B], req_order=req[3][:B],
                         max_members=cnt[2].value, max_shared=cnt[3].value,
@@ -366,6 +369,7 @@ class HostPlan:
     seg_member_slot: np.ndarray
     seg_split_off: np.ndarray
     seg_member_part: np.ndarray
+    seg_items: np.ndarray
     req_num_shared: np.ndarray
     req_num_parts: np.ndarray
     req_private_start: np.ndarray

@@ -545,11 +545,12 @@ radix_status radix_req_finish_batch(radix_tree *tree, const int32_t *tok, const 
 
 radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *nodes,
                                     int32_t batch, int32_t min_members, int32_t split_keys,
-                                    int32_t cap_seg, int32_t cap_mem, int32_t *seg_row,
-                                    int32_t *seg_start, int32_t *seg_end,
+                                    int32_t cap_seg, int32_t cap_mem, int32_t cap_items,
+                                    int32_t *seg_row, int32_t *seg_start, int32_t *seg_end,
                                     int32_t *seg_member_off, int32_t *seg_members,
                                     int32_t *seg_member_slot, int32_t *seg_split_off,
-                                    int32_t *seg_member_part, int32_t *req_num_shared,
+                                    int32_t *seg_member_part, int32_t *seg_items,
+                                    int32_t *req_num_shared,
                                     int32_t *req_num_parts, int32_t *req_private_start,
                                     int32_t *req_order, int32_t *num_segments,
                                     int32_t *num_member_entries, int32_t *max_members,
@@ -654,11 +655,12 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
   *max_members = maxm;
   *num_seg_items = items;
   *max_seg_splits = maxchunks;
-  RADIX_REQUIRE(static_cast<int32_t>(segs.size()) <= cap_seg && total_mem <= cap_mem,
+  RADIX_REQUIRE(static_cast<int32_t>(segs.size()) <= cap_seg && total_mem <= cap_mem &&
+                    items <= cap_items,
                 "decode plan capacity too small");
   RADIX_REQUIRE(segs.empty() || (seg_row && seg_start && seg_end && seg_member_off &&
                                  seg_members && seg_member_slot && seg_split_off &&
-                                 seg_member_part),
+                                 seg_member_part && seg_items),
                 "null output pointer");
   int32_t off = 0, chunk_off = 0;
   for (size_t s = 0; s < segs.size(); ++s) {
@@ -667,6 +669,23 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
     seg_end[s] = segs[s].end;
     seg_member_off[s] = off;
     seg_split_off[s] = chunk_off;
+    // chunk k covers [start + k*clen, min(end, start + (k+1)*clen)), clen = the
+    // segment's length over its chunk count rounded up to 64 keys (one key tile);
+    // trailing chunks may be empty
+    const int32_t len = segs[s].end - segs[s].start, pieces = segs[s].chunks;
+    const int32_t clen = ((len + pieces - 1) / pieces + 63) / 64 * 64;
+    for (int32_t k = 0; k < pieces; ++k) {
+      int32_t *r = seg_items + static_cast<int64_t>(chunk_off + k) * 8;
+      const int64_t lo = std::min<int64_t>(segs[s].end, segs[s].start + static_cast<int64_t>(k) * clen);
+      r[0] = static_cast<int32_t>(lo);
+      r[1] = static_cast<int32_t>(std::min<int64_t>(segs[s].end, lo + clen));
+      r[2] = off;
+      r[3] = static_cast<int32_t>(segs[s].members.size());
+      r[4] = segs[s].row;
+      r[5] = static_cast<int32_t>(s);
+      r[6] = k;
+      r[7] = 0;
+    }
     chunk_off += segs[s].chunks;
     for (auto &m : segs[s].members) {
       seg_members[off] = m.b;

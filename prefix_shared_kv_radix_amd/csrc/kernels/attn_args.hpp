@@ -58,6 +58,8 @@ struct AttnArgs {
   // key chunks of segment s: seg_split_off[s] .. seg_split_off[s+1]-1; a member's partial
   // of chunk k of its segment is seg_member_part[entry] + k
   const int32_t *seg_split_off, *seg_member_part;
+  // one record per chunk: {lo, hi, member offset, member count, row, segment, chunk, 0}
+  const int32_t *seg_items;
   int num_segments;
   const int32_t *req_num_parts;   // segment partials of each request (NULL: none)
   int num_splits;   // private splits per request

@@ -356,7 +356,8 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   if (use_plan) {
     REQUIRE(plan->seg_row && plan->seg_start && plan->seg_end && plan->seg_member_off &&
                 plan->seg_members && plan->seg_member_slot && plan->seg_split_off &&
-                plan->seg_member_part && plan->req_num_shared && plan->req_num_parts &&
+                plan->seg_member_part && plan->seg_items && plan->req_num_shared &&
+                plan->req_num_parts &&
                 plan->req_private_start && plan->num_member_entries > 0 &&
                 plan->max_members > 0 && plan->max_shared > 0 &&
                 plan->num_seg_items >= plan->num_segments && plan->max_parts >= plan->max_shared &&
@@ -464,6 +465,7 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     a.seg_member_slot = plan->seg_member_slot;
     a.seg_split_off = plan->seg_split_off;
     a.seg_member_part = plan->seg_member_part;
+    a.seg_items = plan->seg_items;
     a.num_segments = plan->num_segments;
     a.req_num_parts = plan->req_num_parts;
     a.private_start = plan->req_private_start;

@@ -179,16 +179,17 @@ __device__ __forceinline__ void valu_body(const AttnArgs &a, int w, int n_items,
     pieces = a.seg_split_off[sg + 1] - a.seg_split_off[sg];
     if (split >= pieces) return;
     b = a.seg_members[item];
-    lo = a.seg_start[sg];
-    hi = a.seg_end[sg];
+    const int32_t *rec = a.seg_items + static_cast<int64_t>(a.seg_split_off[sg] + split) * 8;
+    lo = rec[0];   // the chunk's own key range (below, split 0 of one chunk)
+    hi = rec[1];
     q_row = b;
-    rtt_row = rtt_row_of(a, a.seg_row[sg]);
+    rtt_row = rtt_row_of(a, rec[4]);
     part = a.seg_member_part[item] + split;
   }
   // TAIL: common chunk length (a.split_chunk) so uneven requests spread evenly;
-  // MODE 2: the segment's own length cut into its chunk count
-  const int chunk = (TAIL && nsplit > 1) ? a.split_chunk : ((hi - lo + pieces - 1) / pieces + 15) & ~15;
-  const int s_lo = lo + split * chunk;
+  // MODE 2: [lo, hi) is already this chunk
+  const int chunk = (TAIL && nsplit > 1) ? a.split_chunk : ((hi - lo + 15) & ~15);
+  const int s_lo = lo + (MODE == 2 ? 0 : split * chunk);
   const int s_hi = min(hi, s_lo + chunk);
 
   const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * D * sizeof(T);
@@ -910,18 +911,16 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     hi = P + i_last + 1;
     rtt_row = rtt_row_of(a, b);
   } else {
-    // item = key chunk: chunk ks of segment sg (the segment's own chunk count)
-    const int sg = find_owner(a.seg_split_off, a.num_segments, item);
-    ks = item - a.seg_split_off[sg];
-    const int pieces = a.seg_split_off[sg + 1] - a.seg_split_off[sg];
-    mem_off = a.seg_member_off[sg];
-    nrows = (a.seg_member_off[sg + 1] - mem_off) * G;
+    // item = one key chunk of a segment: its record gives the key range, members and
+    // slot row in one (uniform) load
+    const int32_t *rec = a.seg_items + static_cast<int64_t>(item) * 8;
+    lo = rec[0];
+    hi = rec[1];
+    mem_off = rec[2];
+    nrows = rec[3] * G;
+    ks = rec[6];
     if (tile * MF_BM >= nrows) return;
-    const int s0 = a.seg_start[sg], s1 = a.seg_end[sg];
-    const int chunk = ((s1 - s0 + pieces - 1) / pieces + MF_BN - 1) / MF_BN * MF_BN;
-    lo = s0 + ks * chunk;
-    hi = min(s1, lo + chunk);
-    rtt_row = rtt_row_of(a, a.seg_row[sg]);
+    rtt_row = rtt_row_of(a, rec[4]);
   }
 
   // this lane's query row

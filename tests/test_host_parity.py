@@ -221,6 +221,24 @@ def test_decode_plan_key_chunks():
             np.testing.assert_array_equal(np.diff(plan.seg_split_off), want)
             assert plan.num_seg_items == int(want.sum())
             assert plan.max_seg_splits == (int(want.max()) if len(want) else 0)
+            # chunk records: the chunks of segment s tile [start, end) in order, each at
+            # most one rounded-up share long, with the segment's members and row
+            rec = plan.seg_items.reshape(-1, 8)
+            assert len(rec) == plan.num_seg_items
+            for s_ in range(plan.num_segments):
+                k0, k1 = plan.seg_split_off[s_], plan.seg_split_off[s_ + 1]
+                n_ = int(lens[s_])
+                share = -(-(-(-n_ // (k1 - k0))) // 64) * 64
+                pos = plan.seg_start[s_]
+                for k in range(k0, k1):
+                    r = rec[k]
+                    assert r[0] == pos and pos <= r[1] <= plan.seg_end[s_] and r[1] - r[0] <= share
+                    assert r[1] - r[0] == min(share, plan.seg_end[s_] - pos)
+                    pos = r[1]
+                    assert (r[2], r[3], r[4], r[5], r[6]) == (
+                        plan.seg_member_off[s_], plan.seg_member_off[s_ + 1] - plan.seg_member_off[s_],
+                        plan.seg_row[s_], s_, k - k0)
+                assert pos == plan.seg_end[s_]
             for i in range(len(adm)):
                 owned = []   # (rank, first part, chunks) of request i's segments
                 for s_ in range(plan.num_segments):
