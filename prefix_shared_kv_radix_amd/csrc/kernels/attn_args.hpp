@@ -62,8 +62,9 @@ struct AttnArgs {
   const int32_t *seg_items;
   int num_segments;
   const int32_t *req_num_parts;   // segment partials of each request (NULL: none)
-  int num_splits;   // private splits per request
-  int split_chunk;  // keys per private split (all requests), when num_splits > 1
+  int num_splits;   // private splits of each request at or past whole_reqs
+  int whole_reqs;   // requests [0, whole_reqs) read their private keys as one part
+  int split_chunk;  // keys per private split, when a request has num_splits > 1
   int parts, part_base;  // partial slots per (request, head); private ones start at part_base
   // decode: the new token's K/V (read directly for the last position and stored by the
   // tail kernel) and its slot (appended to the slot list); all NULL when already stored

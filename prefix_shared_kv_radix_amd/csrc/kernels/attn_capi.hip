@@ -94,6 +94,7 @@ AttnArgs attn_args(const radix_attn_shape *s, const radix_kv_buffers *kv, const 
   a.Hkv = s->num_kv_heads;
   a.scale_log2 = s->sm_scale * kLog2e;
   a.num_splits = 1;
+  a.whole_reqs = 0;
   return a;
 }
 
@@ -191,6 +192,35 @@ int private_len_bound(int max_seq_len, const radix_decode_plan *plan) {
   return p < 1 ? 1 : p;
 }
 
+#ifndef RADIX_FUSED_LATE_PCT
+#define RADIX_FUSED_LATE_PCT 25
+#endif
+#ifndef RADIX_FUSED_LATE_SPLITS
+#define RADIX_FUSED_LATE_SPLITS 2
+#endif
+
+// How the private keys of a decode step are cut: requests [0, whole_reqs) in one part,
+// the others in `splits` parts of equal length. A caller's num_splits applies to every
+// request. Automatically, the bf16 step with a plan keeps short tails whole but cuts
+// those of the last requests in launch order: their waves are the ones that start
+// when the first waves finish, and whole tails there leave most of the GPU idle while
+// the last few run.
+struct TailCut {
+  int splits, whole_reqs;
+};
+TailCut tail_cut(const radix_attn_shape *shape, int batch, int max_seq_len,
+                 const radix_decode_plan *plan, int num_splits) {
+  if (num_splits > 0) return {num_splits, num_splits == 1 ? batch : 0};
+  const int plen = private_len_bound(max_seq_len, plan);
+  const int s = auto_splits(batch, shape->num_kv_heads, plen);
+  const bool fused = plan && plan->num_segments > 0 && classify(shape) == Kind::GqaBf16;
+  const int late = batch * RADIX_FUSED_LATE_PCT / 100;
+  if (s > 1 || !fused || late == 0 || RADIX_FUSED_LATE_SPLITS < 2 ||
+      plen < 32 * RADIX_FUSED_LATE_SPLITS)
+    return {s, s == 1 ? batch : 0};
+  return {RADIX_FUSED_LATE_SPLITS, batch - late};
+}
+
 // True if the kernels may read p: device memory, or host memory pinned and mapped into
 // the device's address space at the same address (a pageable pointer would fault).
 bool device_readable(const void *p) {
@@ -272,8 +302,7 @@ radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int
                            (static_cast<size_t>(shape->head_dim_v) + 1) * sizeof(float);
     return RADIX_OK;
   }
-  if (num_splits == 0)
-    num_splits = auto_splits(batch, shape->num_kv_heads, private_len_bound(max_seq_len, plan));
+  num_splits = tail_cut(shape, batch, max_seq_len, plan, num_splits).splits;
   const bool use_plan = plan && plan->num_segments > 0;
   const size_t shared = use_plan ? static_cast<size_t>(plan->max_parts) : 0;
   const size_t parts = shared + static_cast<size_t>(num_splits);
@@ -420,9 +449,8 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     return hip_status(radix_launch::combine(true, c, batch, shape->head_dim_v, s), "combine launch");
   }
 
-  const int splits = num_splits > 0 ? num_splits
-                                    : auto_splits(batch, shape->num_kv_heads,
-                                                  private_len_bound(max_seq_len, plan));
+  const TailCut cut = tail_cut(shape, batch, max_seq_len, use_plan ? plan : nullptr, num_splits);
+  const int splits = cut.splits;
   const int max_shared = use_plan ? plan->max_parts : 0;   // segment partials per request
   const int parts = max_shared + splits;
   const bool direct = !use_plan && splits == 1;
@@ -442,6 +470,7 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   AttnArgs a = attn_args(shape, kv, q, req_to_token, rtt_stride, req_rows, out, lse_out);
   a.seq_lens = seq_lens;
   a.num_splits = splits;
+  a.whole_reqs = cut.whole_reqs;
   {
     const int plen = private_len_bound(max_seq_len, use_plan ? plan : nullptr);
     a.split_chunk = ((plen + splits - 1) / splits + 15) & ~15;

@@ -441,6 +441,15 @@ __device__ __forceinline__ float sum8(float x) {
 // The first four partials of all NR requests are loaded before any is folded, so the
 // merges take one memory round trip rather than one per request. Called by the last
 // producer to arrive, after its counter read.
+// Private parts of request b, and the private-tail items of a step whose first `whole`
+// requests are read in one part and the rest in nsplit parts each.
+__device__ __forceinline__ int tail_parts(const AttnArgs &a, int b) {
+  return b < a.whole_reqs ? 1 : a.num_splits;
+}
+__host__ __device__ __forceinline__ int tail_items(int whole, int n_items, int nsplit, int hkv) {
+  return (whole + (n_items - whole) * nsplit) * hkv;
+}
+
 template <int G, int NR>
 __device__ __forceinline__ void merge_requests_bf16(const AttnArgs &a, const int (&bs)[NR],
                                                     const int (&nparts)[NR], int n, int kvh) {
@@ -457,7 +466,7 @@ __device__ __forceinline__ void merge_requests_bf16(const AttnArgs &a, const int
     auto load4 = [&](int r, int p0) {
       const int b = r < n ? bs[r] : bs[0];
       const int ns = r < n ? nparts[r] : nparts[0];
-      const int total = ns + a.num_splits;
+      const int total = ns + tail_parts(a, b);
       const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -497,7 +506,7 @@ __device__ __forceinline__ void merge_requests_bf16(const AttnArgs &a, const int
       float M = kNegBig, L = 0.f;
       f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = O0;
       fold4(r, M, L, O0, O1);
-      for (int p0 = 4; p0 < nparts[r] + a.num_splits; p0 += 4) {   // more than 4 partials
+      for (int p0 = 4; p0 < nparts[r] + tail_parts(a, b); p0 += 4) {   // more than 4 partials
         load4(r, p0);
         fold4(r, M, L, O0, O1);
       }
@@ -532,23 +541,28 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   asm volatile("" : "+v"(lane));
   const int r8 = lane >> 3, sub = lane & 7;
   w = __builtin_amdgcn_readfirstlane(w);   // one work item per wave: its indices are scalar
-  if (w >= n_items * nsplit * a.Hkv) return;
-  const int kvh = w % a.Hkv;
-  const int split = (w / a.Hkv) % nsplit;
-  const int b = w / (a.Hkv * nsplit);
+  // items: (request, KV head) for the requests read whole, then (request, split, KV head)
+  const int whole = min(a.whole_reqs, n_items);
+  if (w >= tail_items(whole, n_items, nsplit, a.Hkv)) return;
+  const bool one = w < whole * a.Hkv;
+  const int wr = one ? w : w - whole * a.Hkv;
+  const int ns_tail = one ? 1 : nsplit;   // private parts of this request
+  const int kvh = wr % a.Hkv;
+  const int split = (wr / a.Hkv) % ns_tail;
+  const int b = (one ? 0 : whole) + wr / (a.Hkv * ns_tail);
 
   const int hi = a.seq_lens[b];
   const int lo = a.private_start ? a.private_start[b] : 0;
   const int64_t q_row = b;
   const int32_t *rtt_row = rtt_row_of(a, b);
   const int part = a.part_base + split;
-  const int chunk = nsplit > 1 ? a.split_chunk : ((hi - lo + 15) & ~15);
+  const int chunk = ns_tail > 1 ? a.split_chunk : ((hi - lo + 15) & ~15);
   const int s_lo = lo + split * chunk;
   const int s_hi = min(hi, s_lo + chunk);
 
   const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * D * 2;
-  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * D * 2 + sub * 32;
-  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * 2 + sub * 32;
+  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * D * 2 + sub * 16;
+  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * 2 + sub * 16;
   const bool fuse_new = a.k_new != nullptr;
   const char *knew = nullptr, *vnew = nullptr;
   // the new token's slot: read now (new_slots may be pinned host memory), used at the end
@@ -556,21 +570,21 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   const int64_t new_at = static_cast<int64_t>(a.req_rows ? a.req_rows[b] : b) * a.rtt_stride + hi - 1;
   int32_t new_slot = 0;
   if (fuse_new) {
-    const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D * 2 + sub * 32;
+    const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D * 2 + sub * 16;
     knew = reinterpret_cast<const char *>(a.k_new) + off;
     vnew = reinterpret_cast<const char *>(a.v_new) + off;
     if (store_new) new_slot = a.new_slots ? a.new_slots[b] : a.rtt[new_at];
   }
   const int ns_b = a.req_num_parts ? a.req_num_parts[b] : 0;
-  const int expected = ns_b + nsplit;   // producers of this request's output
+  const int expected = ns_b + ns_tail;   // producers of this request's output
 
   // q: G heads x this lane's 16 dims, packed bf16 pairs (unscaled)
   uint32_t qp[G][8];
   {
-    const char *qb = reinterpret_cast<const char *>(a.q) + (q_row * a.Hq + kvh * G) * D * 2 + sub * 32;
+    const char *qb = reinterpret_cast<const char *>(a.q) + (q_row * a.Hq + kvh * G) * D * 2 + sub * 16;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const u32x4 x0 = ldg16(qb + h * D * 2), x1 = ldg16(qb + h * D * 2 + 16);
+      const u32x4 x0 = ldg16(qb + h * D * 2), x1 = ldg16(qb + h * D * 2 + 128);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         qp[h][c] = x0[c];
@@ -606,9 +620,9 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
       const char *kp = kb + static_cast<int64_t>(sl[g]) * row_bytes;
       const char *vp = vb + static_cast<int64_t>(sl[g]) * row_bytes;
       kd[g][0] = ldg16(kp);
-      kd[g][1] = ldg16(kp + 16);
+      kd[g][1] = ldg16(kp + 128);
       vd[g][0] = ldg16(vp);
-      vd[g][1] = ldg16(vp + 16);
+      vd[g][1] = ldg16(vp + 128);
     }
   };
   auto compute = [&](bool valid0, bool valid1, const u32x4 (*kr)[2], const u32x4 (*vr)[2]) {
@@ -690,9 +704,9 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   if (fuse_new && hi - 1 >= s_lo && hi - 1 < s_hi) {   // (uniform) the newest key
     u32x4 kr[2][2], vr[2][2];
     kr[0][0] = ldg16(knew);
-    kr[0][1] = ldg16(knew + 16);
+    kr[0][1] = ldg16(knew + 128);
     vr[0][0] = ldg16(vnew);
-    vr[0][1] = ldg16(vnew + 16);
+    vr[0][1] = ldg16(vnew + 128);
     kr[1][0] = kr[0][0];
     kr[1][1] = kr[0][1];
     vr[1][0] = vr[0][0];
@@ -708,15 +722,15 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     char *kd = const_cast<char *>(kb) + static_cast<int64_t>(new_slot) * row_bytes;
     char *vd = const_cast<char *>(vb) + static_cast<int64_t>(new_slot) * row_bytes;
     *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
-    *reinterpret_cast<u32x4 *>(kd + 16) = ldg16(knew + 16);
+    *reinterpret_cast<u32x4 *>(kd + 128) = ldg16(knew + 128);
     *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
-    *reinterpret_cast<u32x4 *>(vd + 16) = ldg16(vnew + 16);
+    *reinterpret_cast<u32x4 *>(vd + 128) = ldg16(vnew + 128);
   }
   // merge counter of this (request, KV head), read now for the single-chunk fold below
   // so that its round trip overlaps the cross-lane reduction (a stale, lower count only
   // means the ordinary path: own partial and arrival)
   int32_t *cnt = a.merge_cnt + static_cast<int64_t>(b) * a.Hkv + kvh;
-  const bool may_fold = nsplit == 1 && ns_b > 0;
+  const bool may_fold = ns_tail == 1 && ns_b > 0;
   int seen = 0;
   if (may_fold && lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -753,7 +767,7 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     for (int half = 0; half < 2; ++half) {
       if (((2 * h + half) & 7) != r8) continue;
       const int head = kvh * G + h;
-      const int d0 = sub * 16 + half * 8;
+      const int d0 = half * 64 + sub * 8;
       float M = m[h], L = l[h];
       float O[8];
 #pragma unroll
@@ -839,7 +853,7 @@ __device__ __forceinline__ int32_t take_ticket(int32_t *q) {
 template <int G>
 __global__ __launch_bounds__(256, G >= 8 ? 1 : 2) void tail_bf16_kernel(AttnArgs a, int n_items,
                                                                         int nsplit) {
-  const int total = n_items * nsplit * a.Hkv;
+  const int total = tail_items(min(a.whole_reqs, n_items), n_items, nsplit, a.Hkv);
   const int nwaves = static_cast<int>(gridDim.x) * 4;
   int w = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);
   w = __builtin_amdgcn_readfirstlane(w);
@@ -1163,7 +1177,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     if (arriver) {
       const int bq = static_cast<int>(q_tok);
       int32_t *cnt = a.merge_cnt + static_cast<int64_t>(bq) * a.Hkv + kvh;
-      if (arrive(cnt) == np_q + a.num_splits - 1) {
+      if (arrive(cnt) == np_q + tail_parts(a, bq) - 1) {
         reset_counter(cnt);
         last_b = bq;
       }
@@ -1244,7 +1258,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int Dv, int ba
   if (e >= a.Hq * Dv) return;
   const int head = e / Dv, d = e % Dv;
   const int ns = a.req_num_parts ? a.req_num_parts[b] : 0;
-  const int total = ns + a.num_splits;
+  const int total = ns + tail_parts(a, b);
   const int64_t base = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
   float M = kNegBig, L = 0.f;
   f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1318,8 +1332,9 @@ static hipError_t valu_g(int G, int mode, const AttnArgs &a, unsigned items, uns
 
 template <int G>
 static hipError_t launch_tail(const AttnArgs &a, unsigned items, unsigned splits, hipStream_t stream) {
-  const uint64_t waves = static_cast<uint64_t>(items) * splits * a.Hkv;
-  if (waves > 0x7fffffffull) return hipErrorInvalidValue;
+  if (static_cast<uint64_t>(items) * splits * a.Hkv > 0x7fffffffull) return hipErrorInvalidValue;
+  const int whole = a.whole_reqs < static_cast<int>(items) ? a.whole_reqs : static_cast<int>(items);
+  const uint64_t waves = tail_items(whole, static_cast<int>(items), static_cast<int>(splits), a.Hkv);
   if (!a.tail_queue) return hipErrorInvalidValue;
   // blocks resident at once on this device (cached per device)
   static std::atomic<int> resident[64];
@@ -1374,7 +1389,10 @@ template <int G>
 static hipError_t launch_fused(const AttnArgs &a, unsigned tiles, unsigned seg_items,
                                unsigned n_items, unsigned nsplit, hipStream_t s) {
   const uint64_t seg_blocks = 8 * ((static_cast<uint64_t>(tiles) * seg_items * a.Hkv + 7) / 8);
-  const uint64_t tail_blocks = (static_cast<uint64_t>(n_items) * nsplit * a.Hkv + 3) / 4;
+  if (static_cast<uint64_t>(n_items) * nsplit * a.Hkv > 0x7fffffffull) return hipErrorInvalidValue;
+  const int whole = a.whole_reqs < static_cast<int>(n_items) ? a.whole_reqs : static_cast<int>(n_items);
+  const uint64_t tail_blocks =
+      (tail_items(whole, static_cast<int>(n_items), static_cast<int>(nsplit), a.Hkv) + 3ull) / 4;
   if (seg_blocks + tail_blocks > 0x7fffffffull) return hipErrorInvalidValue;
   launch(decode_fused_kernel<G>, dim3(static_cast<unsigned>(seg_blocks + tail_blocks)), dim3(256), 0,
          s, a, tiles, seg_items, n_items, nsplit);

@@ -113,6 +113,14 @@ def test_few_shot_bf16_small(use_plan, splits):
     _run(w, Checker(w), use_plan=use_plan, num_splits=splits)
 
 
+def test_few_shot_bf16_late_private_chunks():
+    """Private tails of 90+ keys: with the plan, the last quarter of the requests read
+    theirs in two chunks while the others fold the shared partials into one; every
+    output of every request."""
+    w = few_shot(5, gqa128_shape(), 200, 16, 90, 4, q_rows=4096)
+    _run(w, Checker(w))
+
+
 @pytest.mark.parametrize("use_plan,splits", [(True, 0), (False, 1), (False, 3)])
 def test_few_shot_bf16_host_slots(use_plan, splits):
     """New decode slots read by the kernel from pinned host memory (no copy launch)."""
