@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,6 +35,25 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 
+# Kernels whose private-tail ring counts its own loads for explicit s_waitcnt: any
+# scratch access (a spill) inside them would shift those counts, so they must not spill.
+NO_SCRATCH = re.compile(r"(tail_bf16_kernel|decode_fused_kernel)ILi[124]E")
+
+
+def _check_scratch(report: str, src: str) -> None:
+    """Reject a build in which a kernel matching NO_SCRATCH uses scratch memory."""
+    name = None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and NO_SCRATCH.search(name) and int(m.group(1)) > 0:
+            raise RuntimeError(f"{src}: {name} spills ({m.group(1)} bytes/lane of scratch); "
+                               "its explicit load waits would be wrong")
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
@@ -49,13 +69,18 @@ def build(verbose: bool = False) -> str:
         jobs.append(["g++", *CXX_FLAGS, "-c", src, "-o", obj])
     for src in sorted(glob.glob(os.path.join(CSRC, "kernels", "*.hip"))):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", src, "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src,
+                     "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
+    for cmd, out in zip(jobs, outs):
+        if cmd[0] == HIPCC:
+            _check_scratch(out, cmd[-3])
     if verbose:
         for o in outs:
-            if o.strip():
-                print(o)
+            for line in o.splitlines():
+                if "remark" not in line:
+                    print(line)
     objs = [j[-1] for j in jobs]
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs])

@@ -608,22 +608,46 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   // last pool row (finite, stored), and their weight is exactly 0.
   const int pool_hi = fuse_new ? min(s_hi, hi - 1) : s_hi;
   const int last = pool_hi - 1;
+  // With up to 4 query heads per KV head the ring's loads are issued as asm and waited
+  // for explicitly: each step waits for exactly the slots it is about to use (the K/V
+  // rows of the step being computed are older, so they have landed too), keeping NB-1
+  // iterations in flight during the arithmetic. The compiler's own wait placement for
+  // this ring also waits for the next iteration's rows (its merge at the loop head is
+  // conservative), which halves the loads in flight. The counts assume that no other
+  // vector memory operation is issued inside the ring, so register spills (scratch
+  // accesses) would break them: the build rejects these kernels if they use scratch.
+  // With 8 heads the kernel spills, and the compiler places the waits.
+  constexpr bool kOwnWaits = G <= 4;
+  static_assert(NB >= 3, "the slot wait covers the rows being computed only for NB >= 3");
   u32x4 kbuf[NB][2][2], vbuf[NB][2][2];
   int32_t sbuf[NB][2];
   auto load_slots = [&](int base, int32_t *sl) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) sl[g] = rtt_row[min(base + 8 * g + r8, last)];
+    for (int g = 0; g < 2; ++g) {
+      const int32_t *p = rtt_row + min(base + 8 * g + r8, last);
+      sl[g] = kOwnWaits ? ld_async4(p) : *p;
+    }
   };
   auto load_kv = [&](const int32_t *sl, u32x4 (*kd)[2], u32x4 (*vd)[2]) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const char *kp = kb + static_cast<int64_t>(sl[g]) * row_bytes;
       const char *vp = vb + static_cast<int64_t>(sl[g]) * row_bytes;
-      kd[g][0] = ldg16(kp);
-      kd[g][1] = ldg16(kp + 128);
-      vd[g][0] = ldg16(vp);
-      vd[g][1] = ldg16(vp + 128);
+      kd[g][0] = kOwnWaits ? ld_async16<0>(kp) : ldg16(kp);
+      kd[g][1] = kOwnWaits ? ld_async16<128>(kp) : ldg16(kp + 128);
+      vd[g][0] = kOwnWaits ? ld_async16<0>(vp) : ldg16(vp);
+      vd[g][1] = kOwnWaits ? ld_async16<128>(vp) : ldg16(vp + 128);
     }
+  };
+  // wait until at most N loads are outstanding; sl and the rows of one ring stage are
+  // tied to the wait so that no use of them is scheduled before it
+  auto wait_ring = [&](auto n, int32_t *sl, u32x4 (*kd)[2], u32x4 (*vd)[2]) {
+    if constexpr (kOwnWaits)
+      asm volatile("s_waitcnt vmcnt(%10)"
+                   : "+v"(sl[0]), "+v"(sl[1]), "+v"(kd[0][0]), "+v"(kd[0][1]), "+v"(kd[1][0]),
+                     "+v"(kd[1][1]), "+v"(vd[0][0]), "+v"(vd[0][1]), "+v"(vd[1][0]), "+v"(vd[1][1])
+                   : "n"(decltype(n)::value)
+                   : "memory");
   };
   auto compute = [&](bool valid0, bool valid1, const u32x4 (*kr)[2], const u32x4 (*vr)[2]) {
     float s[2][G];
@@ -686,20 +710,42 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   // early exit inside it makes the compiler rotate the ring through registers that still
   // have loads in flight, which costs a wait for them every step.
   if (pool_hi > s_lo) {   // (uniform) no pool rows: nothing to load
+    // the compiler's loads (q) land before the ring starts, so that it places no wait
+    // for them inside the loop
+    if constexpr (kOwnWaits) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) load_slots(s_lo + 16 * j, sbuf[j]);
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int j = 0; j + 1 < NB; ++j) load_kv(sbuf[j], kbuf[j], vbuf[j]);
+        for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(qp[h][c]));
+    }
+    // issue order, the same before and inside the loop: step t loads the slots of
+    // iteration t+NB, then the rows of iteration t+NB-1 (whose slots came one step
+    // earlier), then computes iteration t
+    load_slots(s_lo, sbuf[0]);
+#pragma unroll
+    for (int j = 1; j < NB; ++j) {
+      load_slots(s_lo + 16 * j, sbuf[j]);
+      if (j == 1) wait_ring(std::integral_constant<int, 2>{}, sbuf[0], kbuf[0], vbuf[0]);
+      else wait_ring(std::integral_constant<int, 10>{}, sbuf[j - 1], kbuf[j - 1], vbuf[j - 1]);
+      load_kv(sbuf[j - 1], kbuf[j - 1], vbuf[j - 1]);
+    }
     for (int base = s_lo; base < pool_hi; base += 16 * NB) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int it = base + 16 * j;
         const int jl = (j + NB - 1) % NB;
         load_slots(it + 16 * NB, sbuf[j]);
+        // younger than the slots of iteration t+NB-1: the rows of t+NB-2 (8 loads) and
+        // the slots just issued (2); the rows of t are older, so they have landed
+        wait_ring(std::integral_constant<int, 10>{}, sbuf[jl], kbuf[j], vbuf[j]);
         load_kv(sbuf[jl], kbuf[jl], vbuf[jl]);
         compute(it + r8 < pool_hi, it + 8 + r8 < pool_hi, kbuf[j], vbuf[j]);
       }
     }
+    // loads past the end are still in flight into the ring: let them land before the
+    // ring's registers can be reused
+#pragma unroll
+    for (int j = 0; j < NB; ++j) wait_ring(std::integral_constant<int, 0>{}, sbuf[j], kbuf[j], vbuf[j]);
   }
   if (fuse_new && hi - 1 >= s_lo && hi - 1 < s_hi) {   // (uniform) the newest key
     u32x4 kr[2][2], vr[2][2];

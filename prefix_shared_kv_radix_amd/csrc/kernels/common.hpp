@@ -63,6 +63,21 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Loads whose completion the compiler does not track: the caller waits for them with
+// an explicit s_waitcnt that names the destination registers (see the private-tail
+// ring). Nothing may read or copy the destination before that wait.
+__device__ __forceinline__ int32_t ld_async4(const int32_t *p) {
+  int32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 ld_async16(const void *p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
+  return v;
+}
+
 // Partial results merged by another block (possibly on another XCD, whose L2 is not
 // kept coherent with this one): written and read with device-scope relaxed atomic
 // accesses, which the compiler emits as sc1 loads/stores (served past the XCD's L2)
