@@ -60,12 +60,11 @@ class Episode:
     def __init__(self, w, use_plan, splits):
         import torch
         from prefix_shared_kv_radix_amd import _lib
-        from prefix_shared_kv_radix_amd.runner import SEG_SPLIT_KEYS, DeviceState, Engine
-        self.torch, self._lib = torch, _lib
+        from prefix_shared_kv_radix_amd.runner import DeviceState, Engine, build_decode_plan
+        self.torch, self._lib, self.build_plan = torch, _lib, build_decode_plan
         self.w, self.use_plan, self.splits = w, use_plan, splits
-        self.split_keys = SEG_SPLIT_KEYS
         # host-only pass: the rounds (and their plans) are deterministic
-        dry = Engine(w, split_keys=self.split_keys).run()
+        dry = Engine(w).run()
         self.rounds = dry.rounds
         dev = "cuda"
         max_batch = max(len(r.admissions) for r in dry.rounds)
@@ -148,7 +147,7 @@ class Episode:
                 raise RuntimeError("episode diverged from its dry run")
             plan_dev, keep = (None, [])
             if ph.n_decode and self.use_plan and B > 1:
-                plan_dev, keep = _lib.device_plan(tree.decode_plan(nodes, 2, self.split_keys), d.device)
+                plan_dev, keep = _lib.device_plan(self.build_plan(tree, nodes, 2), d.device)
             if ph.extend != "host":
                 rtt_pin[:B].copy_(torch.from_numpy(rows))
                 d.rtt[:B].copy_(rtt_pin[:B], non_blocking=True)

@@ -54,10 +54,30 @@ class EpisodeLog:
 
 _TORCH_KV = {"f32": "float32", "bf16": "bfloat16", "fp8": "uint8"}
 
-# Shared segments longer than this many keys are cut into key chunks in the decode plan,
-# each its own unit of work (a 2048-token prefix: 2 chunks; a 4096-token one: 4), so a
-# long shared prefix is not one block's sequential walk while short ones stay whole.
-SEG_SPLIT_KEYS = 1024
+# Shared segments are cut into key chunks in the decode plan, each its own unit of work,
+# so that a long shared prefix is not one block's sequential walk: a round's plan cuts
+# at half its longest segment, at least SEG_CHUNK_MIN and at most SEG_CHUNK_MAX keys per
+# chunk, and keeps segments up to SEG_CHUNK_MIN keys whole. Measured on one MI355X: a
+# 2048-key prefix shared by 256 requests and 4096-key roots shared by 32 requests are
+# both fastest in two chunks; shorter chunks add more per-chunk work (prologue, partial,
+# merge) than they save in chain length.
+SEG_CHUNK_MIN, SEG_CHUNK_MAX = 1024, 2048
+
+
+def seg_split_keys(longest: int) -> int:
+    """split_keys for a plan whose longest shared segment has `longest` keys (0: none)."""
+    if longest <= SEG_CHUNK_MIN:
+        return 0
+    return min(SEG_CHUNK_MAX, max(SEG_CHUNK_MIN, (longest + 1) // 2))
+
+
+def build_decode_plan(tree, nodes, min_members: int = 2, split_keys: Optional[int] = None):
+    """The round's shared-segment plan; split_keys None picks it with seg_split_keys."""
+    if split_keys is not None:
+        return tree.decode_plan(nodes, min_members, split_keys)
+    plan = tree.decode_plan(nodes, min_members, 0)
+    sk = seg_split_keys(plan.max_seg_len)
+    return plan if sk == 0 else tree.decode_plan(nodes, min_members, sk)
 
 
 class DeviceState:
@@ -108,7 +128,7 @@ class Engine:
     def __init__(self, workload, device=None, use_plan: bool = True, num_splits: int = 0,
                  on_extend: Optional[Callable] = None, on_decode: Optional[Callable] = None,
                  min_members: int = 2, host_slots: bool = False,
-                 split_keys: int = SEG_SPLIT_KEYS):
+                 split_keys: Optional[int] = None):
         self.w = workload
         self.pool = _lib.KVPool(workload.pool_slots)
         self.tree = _lib.RadixTree(self.pool)
@@ -171,8 +191,8 @@ class Engine:
             self.dirty.extend(a.row[a.prefix_len:] for a in rnd.admissions)
         if ph.n_decode:
             if self.use_plan and B > 1:
-                rnd.plan = self.tree.decode_plan([a.node for a in rnd.admissions], self.min_members,
-                                                 self.split_keys)
+                rnd.plan = build_decode_plan(self.tree, [a.node for a in rnd.admissions],
+                                             self.min_members, self.split_keys)
             for s in range(ph.n_decode):
                 slots = self.tree.alloc(B)
                 rnd.decode_slots[s] = slots

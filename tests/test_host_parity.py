@@ -258,6 +258,24 @@ def test_decode_plan_key_chunks():
     assert checked > 50
 
 
+def test_segment_chunk_policy():
+    """The runner cuts a round's shared segments at half the longest one (1024..2048
+    keys per chunk): the few-shot 2048-token prefix and the agent 4096-token roots get
+    two chunks each, the 512-token branches stay whole."""
+    from prefix_shared_kv_radix_amd.runner import seg_split_keys
+    assert [seg_split_keys(n) for n in (0, 1024, 1025, 1500, 2048, 4096, 8192)] == \
+        [0, 0, 1024, 1024, 1024, 2048, 2048]
+    for n, chunks in ((2, {2048: 2}), (4, {4096: 2, 512: 1})):
+        log = Engine(config(n)).run()
+        plans = [r.plan for r in log.rounds if r.plan is not None]
+        assert plans
+        for plan in plans:
+            lens = plan.seg_end - plan.seg_start
+            splits = np.diff(plan.seg_split_off)
+            for ln, k in zip(lens, splits):
+                assert chunks[int(ln)] == int(k), (n, ln, k)
+
+
 def test_decode_workspace_covers_late_private_chunks():
     """A bf16 decode step with a plan and one private chunk per request reads the
     private keys of its last quarter of requests (launch order) in two chunks, once
