@@ -8,8 +8,14 @@ attention over shared segments + private tails), and finish them (insert,
 free duplicates, unpin). Query/K/V inputs are staged in HBM before the timed
 region; slot lists are produced inside it by the host tree and copied over.
 
+The attention runs for `--layers` layers (default 4), each with its own K/V pool and
+the same slot lists, as in a model: one layer's keys (about 210 MB in the few-shot
+decode step) are then not still in the 256 MB last-level cache when that layer's next
+step reads them. With --layers 1 consecutive steps re-read one pool and part of it
+comes from that cache. All figures are per layer.
+
 Prints one JSON line. `value` = decode tokens generated per second of episode
-time (whole job); the breakdown, per-kernel event timings (taken over a second,
+time per layer (whole job); the breakdown, per-kernel event timings (taken over a second,
 identical run of the same steps, since an event pair around every launch slows the
 step), the roofline of the dominant kernel and the CPU oracle's rate on a bounded
 sample are included.
@@ -39,6 +45,9 @@ def parse():
     p.add_argument("--config", default="2", help="2 (default), 1, 3A, 3B, 4, 5bf16, 5fp8")
     p.add_argument("--no-plan", action="store_true", help="decode without shared segments")
     p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--layers", type=int, default=4,
+                   help="attention layers per step, each with its own K/V pool (same contents): "
+                        "together they exceed the 256 MB last-level cache, as a model's layers do")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -57,7 +66,7 @@ def workload_of(name):
 class Episode:
     """Pre-staged device inputs for every round of a workload, and one timed pass."""
 
-    def __init__(self, w, use_plan, splits):
+    def __init__(self, w, use_plan, splits, layers=1):
         import torch
         from prefix_shared_kv_radix_amd import _lib
         from prefix_shared_kv_radix_amd.runner import DeviceState, Engine, build_decode_plan
@@ -71,6 +80,13 @@ class Episode:
         self.stride = max(len(r.tokens) + len(r.out_tokens) for r in w.requests)
         self.d = DeviceState(w, dev, max_batch, self.stride)
         d, s = self.d, w.shape
+        # one K/V pool per layer; layers past the first get copies of the first pool's
+        # initial contents, then every layer's extend and decode store their own rows
+        self.layers = layers
+        self.pools = [(d.k_pool, d.v_pool, d.kv_scale)] + [
+            tuple(None if t is None else t.clone() for t in (d.k_pool, d.v_pool, d.kv_scale))
+            for _ in range(layers - 1)]
+        self.kvs = [_lib.make_kv(*p) for p in self.pools]
         self.staged = []
         self.max_ws = 0
         for r_idx, rnd in enumerate(dry.rounds):
@@ -156,13 +172,15 @@ class Episode:
                 marks[-1][1].record()
             if ph.extend != "host" and st["T"]:
                 if ph.extend == "attend":
-                    _lib.attn_extend(d.shape, d.kv, st["q"], st["k_new"], st["v_new"], st["sc_new"],
-                                     d.rtt, None, st["pl_dev"], st["el_dev"], st["cu_dev"], B,
-                                     st["T"], st["max_e"], st["out"], None)
+                    for kv in self.kvs:
+                        _lib.attn_extend(d.shape, kv, st["q"], st["k_new"], st["v_new"], st["sc_new"],
+                                         d.rtt, None, st["pl_dev"], st["el_dev"], st["cu_dev"], B,
+                                         st["T"], st["max_e"], st["out"], None)
                 else:
-                    slots = np.concatenate([rows[b, st["prefix_len"][b]:st["prompt_len"][b]]
-                                            for b in range(B)])
-                    _lib.kv_store(d.shape, d.kv, st["k_new"], st["v_new"], st["sc_new"], d.i32(slots))
+                    slots = d.i32(np.concatenate([rows[b, st["prefix_len"][b]:st["prompt_len"][b]]
+                                                  for b in range(B)]))
+                    for kv in self.kvs:
+                        _lib.kv_store(d.shape, kv, st["k_new"], st["v_new"], st["sc_new"], slots)
             if mark:
                 marks.append(("decode_start", torch.cuda.Event(enable_timing=True)))
                 marks[-1][1].record()
@@ -183,11 +201,12 @@ class Episode:
                     if w.shape.v_is_k_prefix:
                         st["slot_dev"][s].copy_(pin[s], non_blocking=True)
                         slot_arg = st["slot_dev"][s]
-                    _lib.attn_decode(d.shape, d.kv, st["dq"][s], st["dk"][s],
-                                     None if st["dv"] is None else st["dv"][s],
-                                     None if st["dsc"] is None else st["dsc"][s], slot_arg,
-                                     d.rtt, None, st["seq_dev"][s], B, st["seq_max"][s],
-                                     plan_dev, self.splits, st["dout"], None, self.ws, stream)
+                    for kv in self.kvs:
+                        _lib.attn_decode(d.shape, kv, st["dq"][s], st["dk"][s],
+                                         None if st["dv"] is None else st["dv"][s],
+                                         None if st["dsc"] is None else st["dsc"][s], slot_arg,
+                                         d.rtt, None, st["seq_dev"][s], B, st["seq_max"][s],
+                                         plan_dev, self.splits, st["dout"], None, self.ws, stream)
             if mark:
                 marks.append(("round_end", torch.cuda.Event(enable_timing=True)))
                 marks[-1][1].record()
@@ -345,7 +364,10 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}))
         return
     w = workload_of(args.config)
-    ep = Episode(w, not args.no_plan, args.splits)
+    if args.layers < 1:
+        print("--layers must be at least 1", file=sys.stderr)
+        sys.exit(2)
+    ep = Episode(w, not args.no_plan, args.splits, args.layers)
     torch.cuda.synchronize()
     print(f"[bench] staged {w.name}: {len(ep.rounds)} rounds", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -372,7 +394,9 @@ def main():
     _lib.profile_enable(0)
     print(f"[bench] kernel-timed {args.steps} more steps", file=sys.stderr, flush=True)
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # every figure below is per attention layer: an episode runs `layers` of them
+    L = args.layers
+    ms_per_step = (t1 - t0) * 1e3 / args.steps / L
     dec_tokens = sum(st["B"] * st["ph"].n_decode for st in ep.staged)
     ext_tokens = sum(st["T"] for st in ep.staged if st["ph"].extend == "attend")
     ext_ms = dec_ms = 0.0
@@ -380,18 +404,19 @@ def main():
         for i in range(0, len(seq), 3):
             ext_ms += seq[i][1].elapsed_time(seq[i + 1][1])
             dec_ms += seq[i + 1][1].elapsed_time(seq[i + 2][1])
-    ext_ms /= args.steps
-    dec_ms /= args.steps
+    ext_ms /= args.steps * L
+    dec_ms /= args.steps * L
     kern = {}
     for name, t in prof:
         k = kern.setdefault(name, [0, 0.0])
         k[0] += 1
         k[1] += t
-    kernels = {n: {"launches": c // args.steps, "ms_per_step": t / args.steps, "avg_us": 1e3 * t / c}
+    kernels = {n: {"launches": c // (args.steps * L), "ms_per_step": t / (args.steps * L),
+                   "avg_us": 1e3 * t / c}
                for n, (c, t) in kern.items()}
     dom = max(kern, key=lambda n: kern[n][1])
     byt, flop = algorithmic(w, ep, dom)
-    t_dom = kern[dom][1] / args.steps / 1e3          # seconds per episode in that kernel
+    t_dom = kern[dom][1] / (args.steps * L) / 1e3    # seconds per layer-episode in that kernel
     if dom in ("extend_mfma", "mla_decode"):   # dense bf16 contractions: MFMA-bound
         roof = {"bound": "mfma", "achieved": flop / t_dom / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
@@ -400,7 +425,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dom
     roof["avg_launch_us"] = 1e3 * kern[dom][1] / kern[dom][0]
-    roof["algorithmic_bytes_per_launch"] = byt / (kern[dom][0] / args.steps)
+    roof["algorithmic_bytes_per_launch"] = byt / (kern[dom][0] / (args.steps * L))
     roof["traffic"] = measured_traffic(dom, w.name)
     roof["sources"] = kernel_sources_digest()
     # decode-phase aggregate HBM rate over all decode kernels' algorithmic bytes
@@ -423,7 +448,8 @@ def main():
         "config": {"workload": w.name, "pool_slots": w.pool_slots,
                    "q_heads": w.shape.num_q_heads, "kv_heads": w.shape.num_kv_heads,
                    "head_dim": w.shape.head_dim_qk, "decode_tokens_per_step": dec_tokens,
-                   "extend_tokens_per_step": ext_tokens, "shared_segments": not args.no_plan},
+                   "extend_tokens_per_step": ext_tokens, "shared_segments": not args.no_plan,
+                   "layers": L},
         "extend_ms_per_step": ext_ms,
         "decode_ms_per_step": dec_ms,
         "decode_only_tokens_per_s": dec_tokens / (dec_ms / 1e3) if dec_ms else None,
