@@ -164,12 +164,20 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
     const int n = ln & 31, h = ln >> 5, g = ln >> 4, s16 = ln & 15;
     const int vrow = 4 * (g >> 1) + (s16 >> 2);
 
+    // Region-A chunk c = 16q + r of row n sits at n*1024 + 256q + ((r ^ fA(n)) << 4):
+    // the swizzle only touches the low 4 bits, so the score reads need one lane base per
+    // r (8 of them: r = 2i + h) and take q as a constant offset.
+    const uint8_t *kbase[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kbase[i] = T + n * 1024 + (((2 * i + h) ^ fA(n)) << 4);
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int s = 0; s < kHalfQK / 16; ++s) {
-      const int c = (kHalfQK / 8) * HALF + 2 * s + h;   // < 64 exactly when the pair is
-      const int off = (kHalfQK / 8) * HALF + 2 * s < 64 ? offA(n, c) : offB(n, c - 64);
-      const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(T + off);
+      constexpr int c0 = (kHalfQK / 8) * HALF;
+      const int cs = c0 + 2 * s;   // chunk of the h = 0 lanes (even)
+      const bf16x8 ka = cs < 64
+          ? *reinterpret_cast<const bf16x8 *>(kbase[(cs & 15) >> 1] + 256 * (cs >> 4))
+          : *reinterpret_cast<const bf16x8 *>(T + offB(n, cs - 64 + h));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sc, 0, 0, 0);
       if (s % RADIX_MLA_FENCE == RADIX_MLA_FENCE - 1) __builtin_amdgcn_sched_barrier(0);
     }
@@ -223,18 +231,28 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
       for (int e = 0; e < 4; ++e) w[e] = cvt_bf16x2(sc[8 * j + 2 * e], sc[8 * j + 2 * e + 1]);
       pb[j] = __builtin_bit_cast(bf16x8, w);
     }
-    // V^T operands of one value-dim block (4 transposed reads) at a time
+    // V^T operands of one value-dim block (4 transposed reads) at a time. The chunk of
+    // block d is 16q + 4(d % 4) + lane bits with q = 2*HALF + d/4, and rows 16j + vrow
+    // share vrow's swizzle: one lane base per (d % 4, row vrow or vrow + 8), the rest
+    // constant offsets.
     const uint32_t tb = lds_addr(T);
+    const int cl = 2 * (g & 1) + ((s16 & 3) >> 1), hb = (s16 & 1);
+    uint32_t vb[4][2];
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int r = vrow + 8 * p;
+        vb[dm][p] = tb + r * 1024 + (((4 * dm + cl) ^ fA(r)) << 4) + 8 * hb;
+      }
 #pragma unroll
     for (int d = 0; d < kHalfV / 32; ++d) {
-      const int dv0 = kHalfV * HALF + d * 32 + 16 * (g & 1) + 4 * (s16 & 3);
-      const int c = dv0 >> 3, hb = (dv0 >> 2) & 1;
+      const uint32_t q256 = 256u * (2 * HALF + (d >> 2));
       uint32_t ad[4];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int r0 = 16 * j + vrow;
-        ad[2 * j] = tb + offA(r0, c) + 8 * hb;
-        ad[2 * j + 1] = tb + offA(r0 + 8, c) + 8 * hb;
+        ad[2 * j] = vb[d & 3][0] + 16384u * j + q256;
+        ad[2 * j + 1] = vb[d & 3][1] + 16384u * j + q256;
       }
       u32x2 rv[4];
       lds_tr16_x4(rv, ad);
