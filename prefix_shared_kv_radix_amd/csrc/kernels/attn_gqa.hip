@@ -1148,20 +1148,24 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     const int g = lane >> 4, s16 = lane & 15;
     const int vrow0 = 4 * (g >> 1) + (s16 >> 2);
     const uint32_t vbase = lds_addr(Vt);
+    // chunk of value block dvb = 4*dvb + cl, and rows 16q + x (x < 16) share x's swizzle:
+    // one lane base per (dvb, row vrow0 or vrow0 + 8), keys 16q as constant offsets
+    const int cl = 2 * (g & 1) + ((s16 & 3) >> 1), half = s16 & 1;
+    uint32_t vb[4][2];
+#pragma unroll
+    for (int dvb = 0; dvb < 4; ++dvb)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) vb[dvb][p] = vbase + mf_swz(vrow0 + 8 * p, 4 * dvb + cl) + 8 * half;
 #pragma unroll
     for (int d2 = 0; d2 < 2; ++d2) {   // two 32-dim value blocks per batch of reads
       uint32_t ad[16];
 #pragma unroll
-      for (int dd = 0; dd < 2; ++dd) {
-        const int dv0 = (2 * d2 + dd) * 32 + 16 * (g & 1) + 4 * (s16 & 3);
-        const int c = dv0 >> 3, half = (dv0 >> 2) & 1;
+      for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {   // q = 2 * mb + j: keys 16q .. 16q+15 of the tile
-          const int r0 = 16 * q + vrow0;
-          ad[8 * dd + 2 * q] = vbase + mf_swz(r0, c) + 8 * half;
-          ad[8 * dd + 2 * q + 1] = vbase + mf_swz(r0 + 8, c) + 8 * half;
+          ad[8 * dd + 2 * q] = vb[2 * d2 + dd][0] + 4096u * q;
+          ad[8 * dd + 2 * q + 1] = vb[2 * d2 + dd][1] + 4096u * q;
         }
-      }
       u32x2 rv[16];
       lds_tr16_x16(rv, ad);
 #pragma unroll
