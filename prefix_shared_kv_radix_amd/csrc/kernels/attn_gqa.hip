@@ -401,10 +401,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int n_items,
 
 // ------------------------------------------------------------------ bf16 decode tail
 // One wave = one decode query (the G query heads of one KV head) over one key chunk,
-// for bf16 K/V with 128 dims. Eight lanes cover a 256-byte row (32 bytes each), so an
-// iteration of 16 rows gives every lane two rows (r and r+8 of the iteration).
-//   q.k  : v_dot2_f32_bf16 on packed pairs, then a 3-step DPP sum over the 8 lanes
-//   p.v  : p of the two rows packed to bf16, V dims of the two rows paired with byte
+// for bf16 K/V with 128 dims. Sixteen lanes cover a 256-byte row (16 bytes each, so one
+// load instruction reads four whole rows), and an iteration of 16 rows gives every lane
+// four rows (r, r+4, r+8 and r+12 of the iteration).
+//   q.k  : v_dot2_f32_bf16 on packed pairs, then a 4-step DPP sum over the 16 lanes
+//   p.v  : p of two rows packed to bf16, V dims of the two rows paired with byte
 //          permutes, v_dot2_f32_bf16 per dim (fp32 accumulation)
 // The running maximum is refreshed only when some head's tile maximum exceeds it by
 // more than 2^8 (numerator and denominator share the stale maximum, so nothing is lost).
@@ -425,14 +426,6 @@ __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
   const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
 }
-// sum over each group of 8 consecutive lanes (quad_perm [1,0,3,2], [2,3,0,1], half mirror)
-__device__ __forceinline__ float sum8(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
-  return x;
-}
-
 // Merges every partial of up to NR requests (bs[0 .. n-1], wave-uniform, n >= 1; nparts[r]
 // = request bs[r]'s segment-chunk partial count) for the G query heads of KV head kvh
 // into the bf16 output (and lse): lane -> 8 dims of one head, 512 values per pass.
@@ -539,7 +532,9 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   // opaque per call, so that the values derived from the lane index are computed for each
   // item instead of being kept live across the work-queue loop (register pressure)
   asm volatile("" : "+v"(lane));
-  const int r8 = lane >> 3, sub = lane & 7;
+  // 16 lanes per 256-byte row: lane sub holds dims 8*sub .. 8*sub+7 of a row; the four
+  // row groups r4 take rows r4, r4+4, r4+8 and r4+12 of each 16-row iteration
+  const int r4 = lane >> 4, sub = lane & 15;
   w = __builtin_amdgcn_readfirstlane(w);   // one work item per wave: its indices are scalar
   // items: (request, KV head) for the requests read whole, then (request, split, KV head)
   const int whole = min(a.whole_reqs, n_items);
@@ -578,33 +573,30 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   const int ns_b = a.req_num_parts ? a.req_num_parts[b] : 0;
   const int expected = ns_b + ns_tail;   // producers of this request's output
 
-  // q: G heads x this lane's 16 dims, packed bf16 pairs (unscaled)
-  uint32_t qp[G][8];
+  // q: G heads x this lane's 8 dims, packed bf16 pairs (unscaled)
+  uint32_t qp[G][4];
   {
     const char *qb = reinterpret_cast<const char *>(a.q) + (q_row * a.Hq + kvh * G) * D * 2 + sub * 16;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const u32x4 x0 = ldg16(qb + h * D * 2), x1 = ldg16(qb + h * D * 2 + 128);
+      const u32x4 x = ldg16(qb + h * D * 2);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        qp[h][c] = x0[c];
-        qp[h][4 + c] = x1[c];
-      }
+      for (int c = 0; c < 4; ++c) qp[h][c] = x[c];
     }
   }
-  float m[G], l[G], acc[G][16];
+  float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegBig;
     l[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
 
   // Pool rows of this chunk: [s_lo, pool_hi); the newest key (position hi-1, not yet in
   // the pool when fused) is folded in once after the loop from k_new/v_new.
-  // Iteration t covers rows base .. base+15; this lane takes rows base + r8 and
-  // base + 8 + r8. Every load is unconditional: rows past pool_hi re-read the chunk's
+  // Iteration t covers rows base .. base+15; this lane takes rows base + 4k + r4 (k < 4).
+  // Every load is unconditional: rows past pool_hi re-read the chunk's
   // last pool row (finite, stored), and their weight is exactly 0.
   const int pool_hi = fuse_new ? min(s_hi, hi - 1) : s_hi;
   const int last = pool_hi - 1;
@@ -619,87 +611,87 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   // With 8 heads the kernel spills, and the compiler places the waits.
   constexpr bool kOwnWaits = G <= 4;
   static_assert(NB >= 3, "the slot wait covers the rows being computed only for NB >= 3");
-  u32x4 kbuf[NB][2][2], vbuf[NB][2][2];
-  int32_t sbuf[NB][2];
+  u32x4 kbuf[NB][4], vbuf[NB][4];
+  int32_t sbuf[NB][4];
   auto load_slots = [&](int base, int32_t *sl) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int32_t *p = rtt_row + min(base + 8 * g + r8, last);
-      sl[g] = kOwnWaits ? ld_async4(p) : *p;
+    for (int k = 0; k < 4; ++k) {
+      const int32_t *p = rtt_row + min(base + 4 * k + r4, last);
+      sl[k] = kOwnWaits ? ld_async4(p) : *p;
     }
   };
-  auto load_kv = [&](const int32_t *sl, u32x4 (*kd)[2], u32x4 (*vd)[2]) {
+  auto load_kv = [&](const int32_t *sl, u32x4 *kd, u32x4 *vd) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const char *kp = kb + static_cast<int64_t>(sl[g]) * row_bytes;
-      const char *vp = vb + static_cast<int64_t>(sl[g]) * row_bytes;
-      kd[g][0] = kOwnWaits ? ld_async16<0>(kp) : ldg16(kp);
-      kd[g][1] = kOwnWaits ? ld_async16<128>(kp) : ldg16(kp + 128);
-      vd[g][0] = kOwnWaits ? ld_async16<0>(vp) : ldg16(vp);
-      vd[g][1] = kOwnWaits ? ld_async16<128>(vp) : ldg16(vp + 128);
+    for (int k = 0; k < 4; ++k) {
+      const char *kp = kb + static_cast<int64_t>(sl[k]) * row_bytes;
+      const char *vp = vb + static_cast<int64_t>(sl[k]) * row_bytes;
+      kd[k] = kOwnWaits ? ld_async16<0>(kp) : ldg16(kp);
+      vd[k] = kOwnWaits ? ld_async16<0>(vp) : ldg16(vp);
     }
   };
   // wait until at most N loads are outstanding; sl and the rows of one ring stage are
   // tied to the wait so that no use of them is scheduled before it
-  auto wait_ring = [&](auto n, int32_t *sl, u32x4 (*kd)[2], u32x4 (*vd)[2]) {
+  auto wait_ring = [&](auto n, int32_t *sl, u32x4 *kd, u32x4 *vd) {
     if constexpr (kOwnWaits)
-      asm volatile("s_waitcnt vmcnt(%10)"
-                   : "+v"(sl[0]), "+v"(sl[1]), "+v"(kd[0][0]), "+v"(kd[0][1]), "+v"(kd[1][0]),
-                     "+v"(kd[1][1]), "+v"(vd[0][0]), "+v"(vd[0][1]), "+v"(vd[1][0]), "+v"(vd[1][1])
+      asm volatile("s_waitcnt vmcnt(%12)"
+                   : "+v"(sl[0]), "+v"(sl[1]), "+v"(sl[2]), "+v"(sl[3]), "+v"(kd[0]), "+v"(kd[1]),
+                     "+v"(kd[2]), "+v"(kd[3]), "+v"(vd[0]), "+v"(vd[1]), "+v"(vd[2]), "+v"(vd[3])
                    : "n"(decltype(n)::value)
                    : "memory");
   };
-  auto compute = [&](bool valid0, bool valid1, const u32x4 (*kr)[2], const u32x4 (*vr)[2]) {
-    float s[2][G];
+  // rows k = 0..3 of this lane (row base + 4k + r4) with valid flags `vmask` bit k
+  auto compute = [&](int vmask, const u32x4 *kr, const u32x4 *vr) {
+    float s[4][G];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const bool valid = g == 0 ? valid0 : valid1;
+    for (int k = 0; k < 4; ++k) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          d = dot2bf(qp[h][c], kr[g][0][c], d);
-          d = dot2bf(qp[h][4 + c], kr[g][1][c], d);
-        }
-        d = sum8(d);
-        s[g][h] = valid ? d * a.scale_log2 : -INFINITY;
+        for (int c = 0; c < 4; ++c) d = dot2bf(qp[h][c], kr[k][c], d);
+        d = sum16(d);
+        s[k][h] = ((vmask >> k) & 1) ? d * a.scale_log2 : -INFINITY;
       }
     }
     bool grow = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) grow |= fmaxf(s[0][h], s[1][h]) > m[h] + kGrow;
+    for (int h = 0; h < G; ++h)
+      grow |= fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h])) > m[h] + kGrow;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], fmaxf(s[0][h], s[1][h]));
+        const float mn = fmaxf(m[h], fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h])));
         const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
         m[h] = mn;
         l[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
       }
     }
-    uint32_t pp[G];
+    uint32_t pp[2][G];   // probabilities of rows (0, 1) and (2, 3), packed bf16 pairs
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float p0 = __builtin_amdgcn_exp2f(s[0][h] - m[h]);
-      const float p1 = __builtin_amdgcn_exp2f(s[1][h] - m[h]);
-      l[h] += p0 + p1;
-      pp[h] = pack2bf(p0, p1);
+      float p[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p[k] = __builtin_amdgcn_exp2f(s[k][h] - m[h]);
+      l[h] += (p[0] + p[1]) + (p[2] + p[3]);
+      pp[0][h] = pack2bf(p[0], p[1]);
+      pp[1][h] = pack2bf(p[2], p[3]);
     }
-    // pair dim e of row g=0 with dim e of row g=1
+    // pair dim e of row 2i with dim e of row 2i+1
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t a0 = vr[0][c >> 2][c & 3], a1 = vr[1][c >> 2][c & 3];
-      const uint32_t lo2 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // {row0.lo, row1.lo}
-      const uint32_t hi2 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // {row0.hi, row1.hi}
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        acc[h][2 * c] = dot2bf(pp[h], lo2, acc[h][2 * c]);
-        acc[h][2 * c + 1] = dot2bf(pp[h], hi2, acc[h][2 * c + 1]);
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t a0 = vr[2 * i][c], a1 = vr[2 * i + 1][c];
+        const uint32_t lo2 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // {row.lo, row'.lo}
+        const uint32_t hi2 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // {row.hi, row'.hi}
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][2 * c] = dot2bf(pp[i][h], lo2, acc[h][2 * c]);
+          acc[h][2 * c + 1] = dot2bf(pp[i][h], hi2, acc[h][2 * c + 1]);
+        }
       }
-    }
   };
 
   // Step t computes iteration t (buffer t % NB). Before that it issues, in this order,
@@ -716,7 +708,7 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(qp[h][c]));
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qp[h][c]));
     }
     // issue order, the same before and inside the loop: step t loads the slots of
     // iteration t+NB, then the rows of iteration t+NB-1 (whose slots came one step
@@ -725,8 +717,8 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
 #pragma unroll
     for (int j = 1; j < NB; ++j) {
       load_slots(s_lo + 16 * j, sbuf[j]);
-      if (j == 1) wait_ring(std::integral_constant<int, 2>{}, sbuf[0], kbuf[0], vbuf[0]);
-      else wait_ring(std::integral_constant<int, 10>{}, sbuf[j - 1], kbuf[j - 1], vbuf[j - 1]);
+      if (j == 1) wait_ring(std::integral_constant<int, 4>{}, sbuf[0], kbuf[0], vbuf[0]);
+      else wait_ring(std::integral_constant<int, 12>{}, sbuf[j - 1], kbuf[j - 1], vbuf[j - 1]);
       load_kv(sbuf[j - 1], kbuf[j - 1], vbuf[j - 1]);
     }
     for (int base = s_lo; base < pool_hi; base += 16 * NB) {
@@ -736,10 +728,13 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
         const int jl = (j + NB - 1) % NB;
         load_slots(it + 16 * NB, sbuf[j]);
         // younger than the slots of iteration t+NB-1: the rows of t+NB-2 (8 loads) and
-        // the slots just issued (2); the rows of t are older, so they have landed
-        wait_ring(std::integral_constant<int, 10>{}, sbuf[jl], kbuf[j], vbuf[j]);
+        // the slots just issued (4); the rows of t are older, so they have landed
+        wait_ring(std::integral_constant<int, 12>{}, sbuf[jl], kbuf[j], vbuf[j]);
         load_kv(sbuf[jl], kbuf[jl], vbuf[jl]);
-        compute(it + r8 < pool_hi, it + 8 + r8 < pool_hi, kbuf[j], vbuf[j]);
+        int vmask = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vmask |= (it + 4 * k + r4 < pool_hi) << k;
+        compute(vmask, kbuf[j], vbuf[j]);
       }
     }
     // loads past the end are still in flight into the ring: let them land before the
@@ -748,29 +743,26 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     for (int j = 0; j < NB; ++j) wait_ring(std::integral_constant<int, 0>{}, sbuf[j], kbuf[j], vbuf[j]);
   }
   if (fuse_new && hi - 1 >= s_lo && hi - 1 < s_hi) {   // (uniform) the newest key
-    u32x4 kr[2][2], vr[2][2];
-    kr[0][0] = ldg16(knew);
-    kr[0][1] = ldg16(knew + 128);
-    vr[0][0] = ldg16(vnew);
-    vr[0][1] = ldg16(vnew + 128);
-    kr[1][0] = kr[0][0];
-    kr[1][1] = kr[0][1];
-    vr[1][0] = vr[0][0];
-    vr[1][1] = vr[0][1];
-    compute(r8 == 0, false, kr, vr);
+    u32x4 kr[4], vr[4];
+    kr[0] = ldg16(knew);
+    vr[0] = ldg16(vnew);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      kr[k] = kr[0];
+      vr[k] = vr[0];
+    }
+    compute(r4 == 0 ? 1 : 0, kr, vr);
   }
 
   if (queue) *ticket = take_ticket(queue);
   // the new token's row goes to its slot now (no wave reads it: the newest key is taken
   // from k_new/v_new), so its loads and stores overlap the reduction below
-  if (store_new && r8 == 0) {
+  if (store_new && r4 == 0) {
     if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[new_at] = new_slot;
     char *kd = const_cast<char *>(kb) + static_cast<int64_t>(new_slot) * row_bytes;
     char *vd = const_cast<char *>(vb) + static_cast<int64_t>(new_slot) * row_bytes;
     *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
-    *reinterpret_cast<u32x4 *>(kd + 128) = ldg16(knew + 128);
     *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
-    *reinterpret_cast<u32x4 *>(vd + 128) = ldg16(vnew + 128);
   }
   // merge counter of this (request, KV head), read now for the single-chunk fold below
   // so that its round trip overlaps the cross-lane reduction (a stale, lower count only
@@ -780,9 +772,9 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   int seen = 0;
   if (may_fold && lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // merge the 8 row groups (lanes l, l^8, l^16, l^32 hold the same dims)
+  // merge the 4 row groups (lanes l, l^16, l^32 hold the same dims)
 #pragma unroll
-  for (int mask = 8; mask <= 32; mask <<= 1) {
+  for (int mask = 16; mask <= 32; mask <<= 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float mo = shfl_xor_f(m[h], mask), lo_ = shfl_xor_f(l[h], mask);
@@ -791,7 +783,7 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
       l[h] = l[h] * wa + lo_ * wb;
       m[h] = mn;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[h][e] = acc[h][e] * wa + shfl_xor_f(acc[h][e], mask) * wb;
+      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * wa + shfl_xor_f(acc[h][e], mask) * wb;
     }
   }
 
@@ -805,19 +797,17 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     if (fold && lane == 0) reset_counter(cnt);
   }
 
-  // group r8 writes (head, half) pairs r8, r8 + 8, ...: 8 dims each
+  // group r4 writes heads r4, r4 + 4, ...: 8 dims each
   const bool direct = expected == 1 || fold;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (((2 * h + half) & 7) != r8) continue;
+  for (int h = 0; h < G; ++h) {
+      if ((h & 3) != r4) continue;
       const int head = kvh * G + h;
-      const int d0 = half * 64 + sub * 8;
+      const int d0 = sub * 8;
       float M = m[h], L = l[h];
       float O[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) O[e] = acc[h][half * 8 + e];
+      for (int e = 0; e < 8; ++e) O[e] = acc[h][e];
       if (fold) {   // shared partials: o normalised, lse in log2 units
         const int64_t hp = (static_cast<int64_t>(b) * a.Hq + head) * a.parts;
         for (int p0 = 0; p0 < ns_b; p0 += 4) {
