@@ -336,7 +336,7 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
  * every request reads all its keys. A request's private keys are cut into
  * `num_splits` equal chunks of a common length (0 = choose: one chunk when the
  * tails are short and the batch fills the GPU, else 768-key chunks; with a plan and
- * bf16 K/V, one chunk cuts the tails of the last quarter of the batch, once they
+ * bf16 K/V, one chunk cuts the tails of the last tenth of the batch, once they
  * reach 64 keys, in two); all partial results are merged exactly by their
  * log-sum-exp.
  *   q dev [batch, Hq, Dqk]; out dev [batch, Hq, Dv]; lse_out dev [batch, Hq] or NULL;

@@ -193,7 +193,7 @@ int private_len_bound(int max_seq_len, const radix_decode_plan *plan) {
 }
 
 #ifndef RADIX_FUSED_LATE_PCT
-#define RADIX_FUSED_LATE_PCT 25
+#define RADIX_FUSED_LATE_PCT 10
 #endif
 #ifndef RADIX_FUSED_LATE_SPLITS
 #define RADIX_FUSED_LATE_SPLITS 2

@@ -114,10 +114,10 @@ def test_few_shot_bf16_small(use_plan, splits):
 
 
 def test_few_shot_bf16_late_private_chunks():
-    """Private tails of 90+ keys: with the plan, the last quarter of the requests read
-    theirs in two chunks while the others fold the shared partials into one; every
-    output of every request."""
-    w = few_shot(5, gqa128_shape(), 200, 16, 90, 4, q_rows=4096)
+    """Private tails of 90+ keys: with the plan, the last tenth of the requests (3 of
+    30) read theirs in two chunks while the others fold the shared partials into one;
+    every output of every request."""
+    w = few_shot(5, gqa128_shape(), 200, 30, 90, 4, q_rows=4096)
     _run(w, Checker(w))
 
 

@@ -278,24 +278,24 @@ def test_segment_chunk_policy():
 
 def test_decode_workspace_covers_late_private_chunks():
     """A bf16 decode step with a plan and one private chunk per request reads the
-    private keys of its last quarter of requests (launch order) in two chunks, once
+    private keys of its last tenth of requests (launch order) in two chunks, once
     the private tails reach 64 keys: its workspace then holds two private partials per
     request, as with num_splits = 2. fp32 steps, steps without a plan and shorter tails
-    keep one chunk."""
+    keep one chunk, as do batches under 10 (no request in the last tenth)."""
     def plan(min_private_start):
         return _lib.DecodePlan(1, 256, *([None] * len(_lib._PLAN_ARRAYS)), 256, 1, 2048,
                                min_private_start, 2, 2, 2)
     bf16 = _lib.make_shape(32, 8, 128, 128, "bf16", "bf16", False, 0.088)
     f32 = _lib.make_shape(32, 8, 128, 128, "f32", "f32", False, 0.088)
     ws = _lib.decode_workspace_size
-    for batch in (4, 256):
+    for batch in (10, 256):   # at least one request in the last tenth
         long_tail = plan(2048)
         assert ws(bf16, batch, 2048 + 256, long_tail, 0) == ws(bf16, batch, 2048 + 256, long_tail, 2)
         assert ws(bf16, batch, 2048 + 256, long_tail, 0) > ws(bf16, batch, 2048 + 256, long_tail, 1)
         assert ws(bf16, batch, 2048 + 63, long_tail, 0) == ws(bf16, batch, 2048 + 63, long_tail, 1)
         assert ws(f32, batch, 2048 + 256, long_tail, 0) == ws(f32, batch, 2048 + 256, long_tail, 1)
     assert ws(bf16, 256, 1000, None, 0) == ws(bf16, 256, 1000, None, 1)
-    assert ws(bf16, 3, 2048 + 256, plan(2048), 0) == ws(bf16, 3, 2048 + 256, plan(2048), 1)
+    assert ws(bf16, 9, 2048 + 256, plan(2048), 0) == ws(bf16, 9, 2048 + 256, plan(2048), 1)
 
 
 def test_library_exports_every_declared_symbol():
