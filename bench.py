@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -272,16 +273,27 @@ KERNEL_DIR = os.path.join(ROOT, "prefix_shared_kv_radix_amd", "csrc", "kernels")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_sources_digest():
-    """sha256 over the device kernel sources: counter figures taken from another
-    digest describe other code and are not reported."""
+_CODE_TOKEN = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src):
+    """Source text with comments removed and whitespace runs collapsed (string
+    literals kept): what the compiler sees, up to layout."""
+    src = _CODE_TOKEN.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", src)
+    return " ".join(src.split())
+
+
+def kernel_sources_digest(kernel_dir=None):
+    """sha256 over the device kernel sources, comments and layout ignored: counter
+    figures taken from another digest describe other code and are not reported."""
     import hashlib
+    kernel_dir = kernel_dir or KERNEL_DIR
     h = hashlib.sha256()
-    for f in sorted(os.listdir(KERNEL_DIR)):
+    for f in sorted(os.listdir(kernel_dir)):
         if f.endswith((".hip", ".hpp")):
             h.update(f.encode())
-            with open(os.path.join(KERNEL_DIR, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(kernel_dir, f), encoding="utf-8") as fh:
+                h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -772,7 +772,7 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   int seen = 0;
   if (may_fold && lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // merge the 4 row groups (lanes l, l^16, l^32 hold the same dims)
+  // merge the 4 row groups (lanes l, l^16, l^32 and l^48 hold the same dims)
 #pragma unroll
   for (int mask = 16; mask <= 32; mask <<= 1) {
 #pragma unroll
