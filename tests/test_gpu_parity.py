@@ -121,6 +121,15 @@ def test_few_shot_bf16_late_private_chunks():
     _run(w, Checker(w))
 
 
+@pytest.mark.parametrize("use_plan,splits", [(True, 0), (True, 3), (False, 0), (False, 4)])
+def test_few_shot_bf16_one_token_tails(use_plan, splits):
+    """One-token questions: the private tails hold 1 to 5 pool rows, so most rows of a
+    tail wave's 16-row iteration are masked, and with 3 or 4 chunks most chunks are
+    empty; every output of every request."""
+    w = few_shot(6, gqa128_shape(), 200, 24, 1, 5, q_rows=4096)
+    _run(w, Checker(w), use_plan=use_plan, num_splits=splits)
+
+
 @pytest.mark.parametrize("use_plan,splits", [(True, 0), (False, 1), (False, 3)])
 def test_few_shot_bf16_host_slots(use_plan, splits):
     """New decode slots read by the kernel from pinned host memory (no copy launch)."""
