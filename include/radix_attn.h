@@ -66,6 +66,9 @@ typedef struct radix_kv_pool radix_kv_pool;
 
 /* num_slots >= 0. *out receives the new pool. */
 radix_status radix_kv_pool_create(int64_t num_slots, radix_kv_pool **out);
+/* Releases the caller's handle (NULL: no-op). The pool's memory lives on while any tree
+ * created on it is alive and is freed with the last of them, so pool and trees may be
+ * destroyed in either order; the handle must not be used after this call. */
 void radix_kv_pool_destroy(radix_kv_pool *pool);
 /* Take n slots from the head of the free list into out_slots[n]. All or nothing:
  * RADIX_E_NOMEM if fewer than n are free. */
@@ -90,9 +93,11 @@ radix_status radix_kv_pool_free_list(const radix_kv_pool *pool, int32_t *out, in
 typedef struct radix_tree radix_tree;
 typedef int64_t radix_node; /* 0 = root */
 
-/* The tree draws slots from (and returns them to) `pool`, which must outlive it. */
+/* The tree draws slots from (and returns them to) `pool` and keeps the pool's memory
+ * alive until the tree is destroyed (see radix_kv_pool_destroy). */
 radix_status radix_tree_create(radix_kv_pool *pool, radix_tree **out);
-/* Destroys the tree and returns every cached slot to the pool. */
+/* Destroys the tree (NULL: no-op) and returns every cached slot to the pool, then
+ * drops the tree's hold on the pool (freeing it if its handle was destroyed already). */
 void radix_tree_destroy(radix_tree *tree);
 
 /* Length of the longest cached prefix of tok[n]; changes nothing (the match may end
@@ -129,6 +134,7 @@ typedef struct {
   int64_t num_nodes; /* excluding the root */
   int64_t evicted_tokens_total;
   int64_t tick;
+  int64_t pinned_tokens; /* cached tokens on pinned nodes (= cached - evictable) */
 } radix_tree_stats;
 radix_status radix_tree_stats_get(const radix_tree *tree, radix_tree_stats *out);
 

@@ -39,7 +39,8 @@ class NoMemory(RadixError):
 
 class TreeStats(C.Structure):
     _fields_ = [("cached_tokens", C.c_int64), ("evictable_tokens", C.c_int64),
-                ("num_nodes", C.c_int64), ("evicted_tokens_total", C.c_int64), ("tick", C.c_int64)]
+                ("num_nodes", C.c_int64), ("evicted_tokens_total", C.c_int64), ("tick", C.c_int64),
+                ("pinned_tokens", C.c_int64)]
 
 
 class AttnShape(C.Structure):

@@ -16,6 +16,7 @@
 #include "radix_host.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <new>
 
@@ -309,6 +310,9 @@ radix_tree_stats RadixTree::stats() const {
   s.num_nodes = num_nodes_;
   s.evicted_tokens_total = evicted_total_;
   s.tick = tick_;
+  // a pin covers every ancestor, so an unpinned node has no pinned descendant: every
+  // cached token is either on a pinned node or evictable
+  s.pinned_tokens = cached_ - evictable_;
   return s;
 }
 
@@ -319,13 +323,22 @@ using radix::RadixTree;
 using radix::set_error;
 using radix::SlotPool;
 
+// A pool is freed when its creator has destroyed it and no tree built on it is left:
+// the creator's handle and every tree each hold one reference, so a tree destroyed
+// after its pool (as a garbage collector may order them) still returns its cached slots
+// into live memory.
 struct radix_kv_pool {
   SlotPool p;
+  std::atomic<int64_t> refs{1};
   explicit radix_kv_pool(int64_t n) : p(n) {}
 };
+static void pool_unref(radix_kv_pool *pool) {
+  if (pool->refs.fetch_sub(1, std::memory_order_acq_rel) == 1) delete pool;
+}
 struct radix_tree {
+  radix_kv_pool *owner;
   RadixTree t;
-  explicit radix_tree(SlotPool *p) : t(p) {}
+  explicit radix_tree(radix_kv_pool *p) : owner(p), t(&p->p) {}
 };
 
 #define RADIX_REQUIRE(cond, msg)  \
@@ -353,7 +366,9 @@ radix_status radix_kv_pool_create(int64_t num_slots, radix_kv_pool **out) {
   return RADIX_OK;
 }
 
-void radix_kv_pool_destroy(radix_kv_pool *pool) { delete pool; }
+void radix_kv_pool_destroy(radix_kv_pool *pool) {
+  if (pool) pool_unref(pool);
+}
 
 radix_status radix_kv_pool_alloc(radix_kv_pool *pool, int64_t n, int32_t *out_slots) {
   RADIX_REQUIRE(pool && (n == 0 || out_slots) && n >= 0, "bad arguments");
@@ -384,7 +399,8 @@ radix_status radix_kv_pool_free_list(const radix_kv_pool *pool, int32_t *out, in
 radix_status radix_tree_create(radix_kv_pool *pool, radix_tree **out) {
   RADIX_REQUIRE(pool && out, "bad arguments");
   try {
-    *out = new radix_tree(&pool->p);
+    *out = new radix_tree(pool);
+    pool->refs.fetch_add(1, std::memory_order_relaxed);
   } catch (const std::bad_alloc &) {
     set_error("host allocation failed");
     return RADIX_E_NOMEM;
@@ -392,7 +408,12 @@ radix_status radix_tree_create(radix_kv_pool *pool, radix_tree **out) {
   return RADIX_OK;
 }
 
-void radix_tree_destroy(radix_tree *tree) { delete tree; }
+void radix_tree_destroy(radix_tree *tree) {
+  if (!tree) return;
+  radix_kv_pool *owner = tree->owner;
+  delete tree;   // gives the cached slots back to the owner's pool
+  pool_unref(owner);
+}
 
 radix_status radix_tree_peek(const radix_tree *tree, const int32_t *tok, int64_t n,
                              int64_t *matched) {

@@ -125,6 +125,45 @@ def test_tree_nomem_leaves_state_unchanged():
     assert len(t.alloc(10)) == 10          # everything evictable now
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_pinned_and_evictable_tokens_match_oracle(seed):
+    """Tree statistics while requests are running: pinned tokens (on nodes with a
+    nonzero reference count) and evictable tokens equal the oracle's sums over its
+    nodes, after every admit and finish of a random interleaving."""
+    from oracle import radix as O
+    rng = random.Random(seed)
+    p = _lib.KVPool(400)
+    t = _lib.RadixTree(p)
+    op_ = O.SlotPool(400)
+    ot = O.RadixTree(op_)
+    running = []
+    for _ in range(60):
+        if running and (rng.random() < 0.45 or len(running) > 6):
+            (toks, row, m, node), (orow, om, onode) = running.pop(rng.randrange(len(running)))
+            t.finish(toks, row, m, node)
+            c = ot.insert(toks, orow)
+            op_.release(orow[om:c])
+            ot.unlock(onode)
+        else:
+            toks = np.array([rng.randint(0, 2) for _ in range(rng.randint(1, 12))], np.int32)
+            try:
+                m, row, node = t.admit(toks)
+            except _lib.NoMemory:
+                continue
+            om, oslots, onode = ot.match(toks)
+            ot.lock(onode)
+            new = ot.alloc(len(toks) - om)
+            assert new is not None
+            orow = list(oslots) + list(new)
+            assert m == om and row.tolist() == orow
+            running.append(((toks, row, m, node), (orow, om, onode)))
+        st = t.stats()
+        pinned = sum(len(n.key) for n in ot.nodes() if n.lock > 0)
+        assert st.pinned_tokens == pinned
+        assert st.evictable_tokens == ot.evictable_tokens()
+        assert st.cached_tokens == ot.cached_tokens()
+
+
 def test_unlock_below_zero_and_bad_handles():
     p = _lib.KVPool(10)
     t = _lib.RadixTree(p)
