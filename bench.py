@@ -43,7 +43,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=3)
     p.add_argument("--warmup", type=int, default=1)
-    p.add_argument("--config", default="2", help="2 (default), 1, 3A, 3B, 4, 5bf16, 5fp8")
+    p.add_argument("--config", default="4",
+                   help="4 (default: agent branching, the largest single-GPU workload), "
+                        "1, 2, 3A, 3B, 5bf16, 5fp8")
     p.add_argument("--no-plan", action="store_true", help="decode without shared segments")
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--layers", type=int, default=4,
@@ -323,36 +325,97 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, seconds):
-    """The oracle as it stands, on a bounded sample: decode attention of the
-    workload's decode requests at their first step, request after request."""
+def _oracle_threads():
     from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+
+def _decode_queries(w, log, seconds):
+    """Oracle decode queries of the workload's decode requests, step after step, for
+    at most `seconds`: (queries, elapsed seconds, context length of the first)."""
     from oracle.attention import reference_outputs
-    from oracle.episode import run_episode
-    t0 = time.perf_counter()
-    log = run_episode(w)
-    t_host = time.perf_counter() - t0
     dec = [(a, len(rnd.decode_slots)) for rnd in log.rounds for a in rnd.admissions
            if len(rnd.decode_slots)]
     n = 0
     t0 = time.perf_counter()
-    steps = max(s for _, s in dec)
-    for step in range(steps):
+    for step in range(max(s for _, s in dec)):
         for a, ns in dec:
             if step < ns:
                 reference_outputs(w, a.rid, np.array([a.prompt_len + step]))
                 n += 1
             if time.perf_counter() - t0 > seconds:
-                break
-        if time.perf_counter() - t0 > seconds:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+                return n, time.perf_counter() - t0, int(dec[0][0].prompt_len) + 1
+    return n, time.perf_counter() - t0, int(dec[0][0].prompt_len) + 1
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, on bounded samples of the same workload:
+      - decode: fp64 decode queries of the decode requests (first step on), request
+        after request, for `seconds` with the host's BLAS threads and for a quarter
+        of that on one thread;
+      - extend: the last extended request's new rows against its cached prefix;
+      - host tree: one whole episode of matching, pinning, allocation with eviction,
+        scheduling and insertion, the Python oracle against the C++ library.
+    `value` is the multi-threaded decode rate."""
+    from threadpoolctl import threadpool_limits
+    from oracle.attention import reference_outputs
+    from oracle.episode import run_episode
+    from prefix_shared_kv_radix_amd.runner import Engine
+    w.kv_table()
+    w.q_table()   # built once, outside every timed sample
+    t0 = time.perf_counter()
+    log = run_episode(w)
+    t_py = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Engine(w).run()
+    t_cpp = time.perf_counter() - t0
+    threads = _oracle_threads()
+    n, dt, ctx = _decode_queries(w, log, seconds)
+    with threadpool_limits(1):
+        n1, dt1, _ = _decode_queries(w, log, seconds / 4)
+    ext = [a for rnd in log.rounds for a in rnd.admissions
+           if w.phases[rnd.phase].extend == "attend" and a.prompt_len > a.prefix_len]
+    ext_rate, ext_desc = None, "none"
+    if ext:
+        a = ext[-1]
+        pos = np.arange(a.prefix_len, a.prompt_len)
+        t0 = time.perf_counter()
+        reference_outputs(w, a.rid, pos)
+        te = time.perf_counter() - t0
+        ext_rate = len(pos) / te
+        ext_desc = f"{len(pos)} rows on a {a.prefix_len}-token prefix in {te:.2f}s"
     return {"value": n / dt, "unit": "decode tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} decode queries (from step 0 on, L~{int(dec[0][0].prompt_len) + 1}) of "
-                      f"{w.name} in {dt:.1f}s, fp64 exact attention; oracle tree+pool episode "
-                      f"{t_host:.2f}s",
+            "sample": f"{n} decode queries (from step 0 on, L~{ctx}) of {w.name} in {dt:.1f}s, "
+                      f"fp64 exact attention, {threads} BLAS threads",
+            "single_thread": {"value": n1 / dt1, "unit": "decode tokens/s",
+                              "sample": f"{n1} decode queries in {dt1:.1f}s on one thread"},
+            "extend": {"value": ext_rate, "unit": "extend tokens/s", "sample": ext_desc},
+            "host_tree": {"python_oracle_s": t_py, "cpp_library_s": t_cpp,
+                          "speedup": t_py / t_cpp if t_cpp > 0 else None,
+                          "sample": f"one {w.name} episode: admit (match, pin, alloc with "
+                                    f"eviction), schedule, decode-slot allocation, insert"},
             "host_cores_visible": len(os.sched_getaffinity(0))}
+
+
+def copy_bandwidth(mib=1024, reps=10):
+    """Device-to-device copy rate (read + write bytes per second) of a plain copy of
+    `mib` MiB, median of `reps` event-timed copies: the practical HBM ceiling next to
+    the nominal 8 TB/s."""
+    import torch
+    n = mib << 20
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        y.copy_(x)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    del x, y
+    return 2.0 * n / float(np.median(times)) / 1e9
 
 
 def main():
@@ -435,6 +498,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": byt / t_dom / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    copy_gbps = copy_bandwidth()
+    if roof["bound"] == "hbm":
+        roof["copy_gbps"] = copy_gbps
+        roof["frac_of_copy"] = roof["achieved"] / copy_gbps
     roof["kernel"] = dom
     roof["avg_launch_us"] = 1e3 * kern[dom][1] / kern[dom][0]
     roof["algorithmic_bytes_per_launch"] = byt / (kern[dom][0] / (args.steps * L))
@@ -469,6 +536,8 @@ def main():
         "extend_tflops": ext_flops / (ext_ms / 1e3) / 1e12 if ext_ms else None,
         "decode_algorithmic_gbps": dec_bytes / (dec_ms / 1e3) / 1e9 if dec_ms else None,
         "decode_hbm_frac_of_peak": dec_bytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBPS if dec_ms else None,
+        "copy_gbps": copy_gbps,
+        "extend_mfma_frac_of_peak": ext_flops / (ext_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS if ext_ms else None,
         "kernels": kernels,
         "roofline": roof,
     }

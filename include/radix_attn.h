@@ -289,7 +289,14 @@ typedef struct {
  *       Hq = 128, v_is_k_prefix = 1                              (decode, store)  */
 radix_status radix_attn_supported(const radix_attn_shape *shape, int is_decode);
 
-/* Store K/V rows (one per token, all KV heads) at their slots:
+/* Store K/V rows (one per token, all KV heads) at their slots. Defining passages: the
+ * K/V of every processed token is kept in a cache and reused instead of recomputed
+ * (AWS blog "Improve performance of Falcon models with Amazon SageMaker", section on
+ * the KV cache); each radix-tree edge holds the K/V of its tokens (page "49 ·
+ * RadixAttention, eviction và cache churn", §2). fp8: KV Cache FP8 with one scale per
+ * token (SGLang feature article, §一).
+ * Errors: E_UNSUPPORTED for a shape outside the compiled set, E_INVAL for missing
+ * buffers or a negative count; nothing is launched then. Async on `stream`:
  * k_pool[slots[t]] = k_new[t], v_pool[slots[t]] = v_new[t], kv_scale[slots[t]] = scale_new[t].
  * k_new dev [T, Hkv, Dqk], v_new dev [T, Hkv, Dv] (ignored when v_is_k_prefix),
  * scale_new dev [T] (FP8 only). Slots must be distinct and < num_slots. */
@@ -297,7 +304,9 @@ radix_status radix_kv_store(const radix_attn_shape *shape, const radix_kv_buffer
                             const void *k_new, const void *v_new, const float *scale_new,
                             const int32_t *slots, int64_t num_tokens, void *stream);
 
-/* Workspace bytes radix_attn_decode needs for `batch` requests of at most
+/* Workspace bytes radix_attn_decode needs (split-KV partial results and, for bf16, the
+ * merge counters; the split-and-merge of a long key range follows from the exact
+ * log-sum-exp merge of softmax partials) for `batch` requests of at most
  * `max_seq_len` tokens with `plan` (NULL = no shared segments; only its host
  * fields are read: num_segments, max_parts, min_private_start) and
  * `num_splits` private splits (0 = the count radix_attn_decode chooses itself).
@@ -308,6 +317,13 @@ radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int
                                               int32_t num_splits, size_t *bytes);
 
 /* Extend attention (prefill of new tokens against each request's cached prefix).
+ * Defining passages: prefill processes all of a prompt's tokens at once
+ * (AWS blog "Improve performance of Falcon models with Amazon SageMaker", sections on
+ * the KV cache and on prefill vs decode); only the part after the cached prefix is
+ * computed, the shared part being reused (page "49 · RadixAttention, eviction và
+ * cache churn", §2). Errors: E_UNSUPPORTED (shape not compiled, or MLA), E_INVAL
+ * (missing buffers, negative sizes, max_extend > total_extend); nothing is launched.
+ * No workspace: each 128-row query tile reads the whole key range itself.
  * Request b (rows req_rows[b] of req_to_token, or b when req_rows is NULL) has
  * prefix_lens[b] cached tokens and extend_lens[b] new ones; its new tokens are
  * rows cu_extend[b] .. cu_extend[b+1]-1 of q/k_new/v_new/out. New token i sits
@@ -328,7 +344,12 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
                                const int32_t *cu_extend, int32_t batch, int32_t total_extend,
                                int32_t max_extend, void *out, float *lse_out, void *stream);
 
-/* Decode attention: request b's query (position seq_lens[b]-1) attends keys
+/* Decode attention, one new token per request per step over the cached keys
+ * (AWS blog "Improve performance of Falcon models with Amazon SageMaker", sections on
+ * the KV cache and on continuous batching; decode cost is KV memory traffic, SGLang
+ * feature article §一). Errors: E_UNSUPPORTED, E_INVAL (missing buffers, bad sizes,
+ * workspace too small, pageable new_slots, incomplete plan); nothing is launched.
+ * Request b's query (position seq_lens[b]-1) attends keys
  * 0 .. seq_lens[b]-1 read through req_to_token[row]. When new_slots is not NULL,
  * req_to_token[row][seq_lens[b]-1] = new_slots[b] and the new K/V row
  * (k_new/v_new/scale_new dev [batch, Hkv, *]) is stored at that slot; the query

@@ -82,6 +82,14 @@ __device__ __forceinline__ u32x4 ld_async16(const void *p) {
 // kept coherent with this one): written and read with device-scope relaxed atomic
 // accesses, which the compiler emits as sc1 loads/stores (served past the XCD's L2)
 // without any whole-cache writeback or invalidate.
+// The ordering rests on the GFX942 memory model of the LLVM AMDGPU backend's user guide
+// (gfx950 follows it): a monotonic agent-scope load or store is a global load/store with
+// sc1 set, so it is coherent across XCDs; "s_waitcnt vmcnt(0)" returns only once this
+// wave's earlier stores have completed at that scope; and an agent-scope atomic
+// read-modify-write is performed at the same coherence point. A producer therefore
+// stores its partial (sc1), waits for vmcnt(0), then increments the counter; the
+// consumer that reads the final count issues its sc1 loads of the partials only
+// after that atomic has returned, so they see every producer's data.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 // One 16-byte store with the same cache policy (sc1) that a device-scope relaxed atomic
 // store gets: a pair of 8-byte atomic stores reached HBM as partial-line writes, about

@@ -4,21 +4,30 @@ Each case runs a workload's request script through the native tree and the
 gfx950 kernels (extend, shared-segment decode, split-KV decode, combine) and
 compares the outputs with the oracle's exact attention over each request's
 own keys (fp64): max-abs <= 1e-4 for fp32, <= 2e-2 for bf16 I/O with fp32
-accumulation. LSE within 1e-5 / 1e-3, and 1e-2 when the K/V pool is fp8: the
-dequantised E4M3 values are rounded to bf16 MMA operands (relative error up to
-2^-9 per element), which moves a score by at most
-sm_scale * sum_i |q_i k_i| * 2^-9 (about 3e-2 at the MLA shape, 1e-3 typical).
+accumulation; LSE within 1e-5 / 1e-3.
+
+fp8 K/V (E4M3 bytes times a per-token scale): the kernel rounds each dequantised
+element to a bf16 MMA operand (round to nearest even, relative error at most
+2^-8), so a score moves by at most sm_scale * sum_i |q_i k_i| * 2^-8 and the LSE,
+a smooth maximum of the scores, by at most the largest such move over the keys it
+sees. The LSE tolerance of an fp8 row is that bound, computed from the row's own
+query and dequantised keys, on top of the bf16 tolerance.
+
+Decode checks are gathered while the episode runs and computed afterwards, one
+oracle call per request for all its checked positions, on a thread pool.
 """
 import numpy as np
 import pytest
 
 from conftest import gpu_available
-from oracle.attention import reference_outputs
-from workloads import agent_branch, chat_decode, chat_tree, config, few_shot, gqa128_shape, tiny_shape
+from oracle.attention import reference_outputs, request_kv, request_q
+from workloads import (agent_branch, chat_decode, chat_tree, config, few_shot, gqa128_shape,
+                       mixed_hits, tiny_shape)
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": (1e-4, 1e-5), "bf16": (2e-2, 1e-3)}
+BF16_REL = 2.0 ** -8     # bf16 round-to-nearest-even relative error bound
 
 
 def _to_np(t):
@@ -26,8 +35,22 @@ def _to_np(t):
     return t.detach().to("cpu", torch.float32).numpy()
 
 
+def fp8_lse_bound(w, rid, positions):
+    """Per (position, head) bound on the LSE change caused by rounding the request's
+    dequantised fp8 keys to bf16: sm_scale * 2^-8 * max over visible keys j of
+    sum_i |q_i k_ji|."""
+    positions = np.asarray(positions, dtype=np.int64)
+    L = int(positions.max()) + 1
+    k, _ = request_kv(w, w.full_kv_ids(rid)[:L])                 # [L, 1, Dqk]
+    q = request_q(w, rid, positions)                              # [n, Hq, Dqk]
+    s = np.abs(q) @ np.abs(k[:, 0, :]).T                          # [n, Hq, L]
+    vis = np.arange(L)[None, None, :] <= positions[:, None, None]
+    return w.shape.sm_scale * BF16_REL * 1.01 * np.where(vis, s, 0.0).max(axis=2)
+
+
 class Checker:
-    """Collects device outputs through the runner's callbacks and checks a sample."""
+    """Collects device outputs through the runner's callbacks and checks them against
+    the oracle: extend samples at once, decode outputs after the episode."""
 
     def __init__(self, w, extend_sample=None, decode_steps=None, decode_sample=None, seed=0):
         self.w = w
@@ -36,23 +59,26 @@ class Checker:
         self.decode_steps = decode_steps
         self.decode_sample = decode_sample
         self.tol_o, self.tol_l = TOL[w.shape.q_dtype]
-        if w.shape.kv_dtype == "fp8":
-            self.tol_l = 1e-2
+        self.fp8 = w.shape.kv_dtype == "fp8"
         self.worst = 0.0
         self.checked = 0
+        self.pending = {}   # rid -> [(position, o, lse)]
 
     def _pick(self, n, k):
         if k is None or k >= n:
             return np.arange(n)
         return np.sort(self.rng.choice(n, size=k, replace=False))
 
-    def _cmp(self, o, l, ref_o, ref_l, what):
+    def _cmp(self, rid, pos, o, l, ref_o, ref_l, what):
         err = np.abs(o - ref_o).max()
-        lerr = np.abs(l - ref_l).max()
+        lerr = np.abs(l - ref_l)
+        tol_l = self.tol_l
+        if self.fp8:
+            tol_l = self.tol_l + fp8_lse_bound(self.w, rid, pos)
         self.worst = max(self.worst, err)
         self.checked += 1
         assert err <= self.tol_o, f"{what}: output max-abs {err}"
-        assert lerr <= self.tol_l, f"{what}: lse max-abs {lerr}"
+        assert np.all(lerr <= tol_l), f"{what}: lse max-abs {lerr.max()} (bound {np.min(tol_l)})"
 
     def on_extend(self, rnd, out, lse, cu):
         if out is None:
@@ -67,7 +93,7 @@ class Checker:
                 pos = np.unique(np.concatenate([pos[:8], pos[-8:], self.rng.choice(pos, 24)]))
             ro, rl = reference_outputs(self.w, a.rid, pos)
             idx = cu[b] + (pos - a.prefix_len)
-            self._cmp(o_all[idx], l_all[idx], ro, rl, f"extend rid {a.rid}")
+            self._cmp(a.rid, pos, o_all[idx], l_all[idx], ro, rl, f"extend rid {a.rid}")
 
     def on_decode(self, rnd, step, out, lse):
         if self.decode_steps is not None and step not in self.decode_steps:
@@ -75,9 +101,27 @@ class Checker:
         o_all, l_all = _to_np(out), _to_np(lse)
         for b in self._pick(len(rnd.admissions), self.decode_sample):
             a = rnd.admissions[b]
-            pos = np.array([a.prompt_len + step])
-            ro, rl = reference_outputs(self.w, a.rid, pos)
-            self._cmp(o_all[b:b + 1], l_all[b:b + 1], ro, rl, f"decode rid {a.rid} step {step}")
+            self.pending.setdefault(a.rid, []).append((a.prompt_len + step, o_all[b], l_all[b]))
+
+    def finish(self):
+        """Oracle for every gathered decode output (all of a request's positions in one
+        call), on host threads."""
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        items = sorted(self.pending.items())
+        self.pending = {}
+
+        def one(item):
+            rid, rows = item
+            pos = np.array([p for p, _, _ in rows])
+            ro, rl = reference_outputs(self.w, rid, pos)
+            return rid, pos, rows, ro, rl
+
+        with threadpool_limits(1), ThreadPoolExecutor(16) as ex:
+            for rid, pos, rows, ro, rl in ex.map(one, items):
+                o = np.stack([x[1] for x in rows])
+                l = np.stack([x[2] for x in rows])
+                self._cmp(rid, pos, o, l, ro, rl, f"decode rid {rid} positions {pos.tolist()}")
 
 
 def _run(w, checker, **kw):
@@ -87,6 +131,7 @@ def _run(w, checker, **kw):
     eng = Engine(w, device="cuda", on_extend=checker.on_extend, on_decode=checker.on_decode, **kw)
     log = eng.run()
     torch.cuda.synchronize()
+    checker.finish()
     assert checker.checked > 0
     print(f"[gpu case] {w.name} ok: {checker.checked} checks, worst {checker.worst:.3g}", flush=True)
     return log
@@ -212,18 +257,20 @@ def test_gqa_groups_bf16():
         _run(w, Checker(w))
 
 
-def test_few_shot_full_size_sampled():
+def test_few_shot_full_size():
     """Config 2 at full size (2048-token prefix x 256 requests x 128 tokens, 128 decode
-    steps at batch 256): sampled requests at sampled steps."""
+    steps at batch 256): every request, head and dim at the first and last decode step;
+    sampled extend rows."""
     w = config(2)
-    _run(w, Checker(w, extend_sample=6, decode_steps={0, 1, 64, 127}, decode_sample=8))
+    _run(w, Checker(w, extend_sample=6, decode_steps={0, 127}))
 
 
-def test_agent_full_size_sampled():
+def test_agent_full_size():
     """Config 4: 16 roots x 4096 (prefill), 128 branches x 512, 512 forks decoding
-    256 steps through two nested shared segments."""
+    256 steps through two nested shared segments: every request at the first and last
+    decode step."""
     w = config(4)
-    _run(w, Checker(w, extend_sample=3, decode_steps={0, 255}, decode_sample=6))
+    _run(w, Checker(w, extend_sample=3, decode_steps={0, 255}))
 
 
 def test_chat_tree_full_size_sampled():
@@ -231,10 +278,54 @@ def test_chat_tree_full_size_sampled():
     _run(w, Checker(w, extend_sample=3))
 
 
-def test_chat_decode_full_size_sampled():
-    """Config 3B: 256 decode requests with 1k-8k contexts scattered by churn."""
+def test_chat_decode_full_size():
+    """Config 3B: 256 decode requests with 1k-8k contexts scattered by churn; more
+    private-tail items than resident waves (the work queue): every request at the
+    first and last decode step."""
     w = config(3, "B")
-    _run(w, Checker(w, decode_steps={0, 31}, decode_sample=8))
+    _run(w, Checker(w, decode_steps={0, 31}))
+
+
+@pytest.mark.parametrize("splits", [8, 11])
+def test_tail_work_queue_bf16(splits):
+    """No plan, forced key splits: 96 requests x 8 KV heads x 8 (or 11) chunks give
+    6144 (8448) private-tail items, three to four times the waves resident at once, so
+    most items are drawn from the work queue; three decode steps reuse one workspace
+    (its ticket counters must be back at zero after each call). Every output."""
+    w = few_shot(31, gqa128_shape(), 600, 96, 40, 3, q_rows=4096)
+    _run(w, Checker(w), use_plan=False, num_splits=splits)
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_eight_heads_per_kv_head_no_plan_bf16(splits):
+    """64 query heads over 8 KV heads (8 per KV head) without a plan: the private-tail
+    kernel's 8-head variant, whole and split; every output."""
+    import dataclasses
+    shape = dataclasses.replace(gqa128_shape(), num_q_heads=64)
+    w = few_shot(9, shape, 170, 10, 23, 3, q_rows=512)
+    _run(w, Checker(w), use_plan=False, num_splits=splits)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extend_batch_with_fully_cached_prompts(dtype):
+    """One extend batch holding two wholly cached prompts (nothing to extend), two
+    partly cached ones and an uncached one; then decode. Every output."""
+    w = mixed_hits(21, gqa128_shape() if dtype == "bf16" else tiny_shape(), 150, 40, 3)
+    ext = {}
+
+    def spy(rnd, out, lse, cu):
+        ext["E"] = [a.prompt_len - a.prefix_len for a in rnd.admissions]
+        chk.on_extend(rnd, out, lse, cu)
+
+    chk = Checker(w)
+    import torch
+    from prefix_shared_kv_radix_amd.runner import Engine
+    print(f"[gpu case] {w.name} {dtype}", flush=True)
+    Engine(w, device="cuda", on_extend=spy, on_decode=chk.on_decode).run()
+    torch.cuda.synchronize()
+    chk.finish()
+    assert 0 in ext["E"] and max(ext["E"]) > 0
+    assert chk.checked > 0
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -257,8 +348,8 @@ def test_mla_splits_and_no_plan(kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_mla_full_size_sampled(kv):
+def test_mla_full_size(kv):
     """Config 5: 256 requests x 4096 context (2048-token prefixes shared by groups of
-    32), 32 decode steps, sampled."""
+    32), 32 decode steps: every request at the first and last step."""
     w = config(5, kv)
-    _run(w, Checker(w, decode_steps={0, 31}, decode_sample=6))
+    _run(w, Checker(w, decode_steps={0, 31}))

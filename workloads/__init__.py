@@ -459,6 +459,33 @@ def mla_groups(seed: int, kv_dtype: str, n_groups: int, group_len: int, per_grou
     return Workload(name, seed, shape, pool, reqs, phases, g.next_id, g.next_id, q_rows)
 
 
+def mixed_hits(seed: int, shape: AttnShape, base_len: int, ext_len: int, n_decode: int,
+               name: str = "mixed_hits", q_rows: int = 4096) -> Workload:
+    """An extend batch mixing fully cached prompts (nothing to extend) with partly
+    cached and uncached ones. Warm phase: prompts A (``base_len`` tokens) and
+    B = A + ``ext_len`` tokens. Then one batch of: A again, B again (both wholly
+    cached), A + a new continuation, B + a new continuation and an unrelated prompt,
+    each decoded ``n_decode`` steps."""
+    g = _Tokens(seed)
+    a_tok, a_ids = g.draw(base_len, set()), g.ids(base_len)
+    firsts: set = set()
+    b_more = g.draw(ext_len, firsts)
+    b_tok, b_ids = np.concatenate([a_tok, b_more]), np.concatenate([a_ids, g.ids(ext_len)])
+    reqs = [_req(0, a_tok, a_ids), _req(1, b_tok, b_ids)]
+    a_more = g.draw(ext_len // 2 + 3, firsts)
+    prompts = [(a_tok, a_ids), (b_tok, b_ids),
+               (np.concatenate([a_tok, a_more]), np.concatenate([a_ids, g.ids(len(a_more))])),
+               (np.concatenate([b_tok, g.draw(ext_len + 5)]), np.concatenate([b_ids, g.ids(ext_len + 5)]))]
+    other = g.draw(base_len // 2 + 7, {int(a_tok[0])})
+    prompts.append((other, g.ids(len(other))))
+    for t, ids in prompts:
+        reqs.append(_req(len(reqs), t, ids, g.draw(n_decode), g.ids(n_decode)))
+    pool = sum(len(r.tokens) for r in reqs) + len(prompts) * n_decode
+    phases = [Phase([0, 1], "fcfs", 1, 0, "attend"),
+              Phase(list(range(2, len(reqs))), "fcfs", len(prompts), n_decode, "attend")]
+    return Workload(name, seed, shape, pool, reqs, phases, g.next_id, g.next_id, q_rows)
+
+
 # --------------------------------------------------------------------------
 # the five configurations
 # --------------------------------------------------------------------------
