@@ -146,6 +146,25 @@ radix_status radix_sched_order(const radix_tree *tree, const int32_t *const *tok
                                const int64_t *len, int64_t n, int32_t policy,
                                int64_t *out_order);
 
+/* Data-parallel routing: which of n_workers workers (one GPU each, each with its own
+ * pool and tree) serves a request of tok[n]. The SGLang feature article gives data
+ * parallel attention (§一: batches spread over independent data-parallel workers, so
+ * KV is not stored twice) and names a cache-aware load balancer (§五, heading only);
+ * the rule below is this library's reading of it.
+ *   policy 0: round robin over *rr_counter (incremented);
+ *   policy 1: cache-aware. If the loads are imbalanced (max - min > balance_abs and
+ *             max > balance_rel * min) the least loaded worker; otherwise the worker
+ *             whose tree holds the longest cached prefix of tok (peek: nothing
+ *             changes), ties to the smaller load, then the lower index;
+ *   policy 2: least loaded (ties: lower index).
+ * loads[n_workers] is the caller's load measure (e.g. requests queued this round).
+ * *out_worker receives the worker, *out_matched (may be NULL) that worker's cached
+ * prefix length. E_INVAL on bad arguments or an unknown policy. */
+radix_status radix_route(const radix_tree *const *trees, int32_t n_workers, const int64_t *loads,
+                         const int32_t *tok, int64_t n, int32_t policy, int64_t balance_abs,
+                         double balance_rel, int64_t *rr_counter, int32_t *out_worker,
+                         int64_t *out_matched);
+
 /* Request lifecycle (page 4 §2, §4).
  * admit: match tok[n], pin the matched path, take n - matched new slots (evicting
  *        as needed). out_row[n] receives the slot of every prompt position

@@ -92,6 +92,8 @@ _SIGS = {
     "radix_tree_stats_get": (C.c_int, [_vp, C.POINTER(TreeStats)]),
     "radix_sched_order": (C.c_int, [_vp, C.POINTER(_i32p), _i64p, C.c_int64, C.c_int32, _i64p]),
     "radix_req_admit": (C.c_int, [_vp, _i32p, C.c_int64, _i32p, _i64p, _i64p]),
+    "radix_route": (C.c_int, [C.POINTER(_vp), C.c_int32, _i64p, _i32p, C.c_int64, C.c_int32,
+                              C.c_int64, C.c_double, _i64p, _i32p, _i64p]),
     "radix_req_finish": (C.c_int, [_vp, _i32p, _i32p, C.c_int64, C.c_int64, C.c_int64, _i64p]),
     "radix_req_admit_batch": (C.c_int, [_vp, _i32p, _i64p, C.c_int64, C.c_int64, _i32p, C.c_int64,
                                         _i64p, _i64p, _i64p]),
@@ -358,6 +360,31 @@ class RadixTree:
                         max_members=cnt[2].value, max_shared=cnt[3].value,
                         num_seg_items=cnt[4].value, max_parts=cnt[5].value,
                         max_seg_splits=cnt[6].value)
+
+
+ROUTE_POLICIES = {"round_robin": 0, "cache_aware": 1, "least_load": 2}
+
+
+class Router:
+    """Data-parallel request routing over several trees (one per worker)."""
+
+    def __init__(self, trees, policy: str, balance_abs: int = 32, balance_rel: float = 1.5):
+        self.trees = list(trees)
+        self.policy = ROUTE_POLICIES[policy]
+        self.balance_abs = int(balance_abs)
+        self.balance_rel = float(balance_rel)
+        self.rr = C.c_int64(0)
+
+    def route(self, tokens, loads):
+        """(worker index, that worker's cached prefix length) for one request."""
+        a, p = _i32(tokens)
+        ld = np.ascontiguousarray(loads, dtype=np.int64)
+        hs = (_vp * len(self.trees))(*[t.h for t in self.trees])
+        wk, m = C.c_int32(), C.c_int64()
+        _check(load().radix_route(hs, len(self.trees), ld.ctypes.data_as(_i64p), p, len(a),
+                                  self.policy, self.balance_abs, self.balance_rel,
+                                  C.byref(self.rr), C.byref(wk), C.byref(m)))
+        return wk.value, m.value
 
 
 @dataclass

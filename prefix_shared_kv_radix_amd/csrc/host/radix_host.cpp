@@ -486,6 +486,51 @@ radix_status radix_sched_order(const radix_tree *tree, const int32_t *const *tok
   return RADIX_OK;
 }
 
+radix_status radix_route(const radix_tree *const *trees, int32_t n_workers, const int64_t *loads,
+                         const int32_t *tok, int64_t n, int32_t policy, int64_t balance_abs,
+                         double balance_rel, int64_t *rr_counter, int32_t *out_worker,
+                         int64_t *out_matched) {
+  RADIX_REQUIRE(trees && n_workers > 0 && loads && out_worker && n >= 0 && (n == 0 || tok),
+                "bad arguments");
+  RADIX_REQUIRE(policy >= 0 && policy <= 2, "unknown routing policy");
+  RADIX_REQUIRE(policy != 0 || rr_counter, "round robin needs its counter");
+  for (int32_t i = 0; i < n_workers; ++i) RADIX_REQUIRE(trees[i], "missing worker tree");
+  int32_t pick = 0;
+  auto least_loaded = [&]() {
+    int32_t best = 0;
+    for (int32_t i = 1; i < n_workers; ++i)
+      if (loads[i] < loads[best]) best = i;
+    return best;
+  };
+  if (policy == 0) {
+    pick = static_cast<int32_t>(*rr_counter % n_workers);
+    ++*rr_counter;
+  } else if (policy == 2) {
+    pick = least_loaded();
+  } else {
+    int64_t lo = loads[0], hi = loads[0];
+    for (int32_t i = 1; i < n_workers; ++i) {
+      lo = std::min(lo, loads[i]);
+      hi = std::max(hi, loads[i]);
+    }
+    if (hi - lo > balance_abs && static_cast<double>(hi) > balance_rel * static_cast<double>(lo)) {
+      pick = least_loaded();
+    } else {
+      int64_t best_m = -1;
+      for (int32_t i = 0; i < n_workers; ++i) {
+        const int64_t m = trees[i]->t.peek(tok, n);
+        if (m > best_m || (m == best_m && loads[i] < loads[pick])) {
+          best_m = m;
+          pick = i;
+        }
+      }
+    }
+  }
+  *out_worker = pick;
+  if (out_matched) *out_matched = trees[pick]->t.peek(tok, n);
+  return RADIX_OK;
+}
+
 radix_status radix_req_admit(radix_tree *tree, const int32_t *tok, int64_t n, int32_t *out_row,
                              int64_t *prefix_len, radix_node *node) {
   RADIX_REQUIRE(tree && prefix_len && node && n >= 0 && (n == 0 || (tok && out_row)),

@@ -153,30 +153,35 @@ class Engine:
     # ------------------------------------------------------------------ host
     def run(self) -> EpisodeLog:
         log = EpisodeLog()
-        w = self.w
-        for p_idx, ph in enumerate(w.phases):
-            waiting = list(ph.rids)
-            while waiting:
-                order = self.tree.sched_order([w.requests[r].tokens for r in waiting], ph.policy)
-                waiting = [waiting[i] for i in order]
-                cand = waiting[:ph.batch_limit]
-                k, rows, pl, nodes = self.tree.admit_batch([w.requests[r].tokens for r in cand],
-                                                           ph.batch_limit, self.row_stride)
-                adm: List[Admission] = [
-                    Admission(rid, int(pl[i]), len(w.requests[rid].tokens),
-                              rows[i, :len(w.requests[rid].tokens)].copy(), int(nodes[i]))
-                    for i, rid in enumerate(cand[:k])]
-                if not adm:
-                    raise RuntimeError(f"request {waiting[0]} cannot be admitted into an idle pool")
-                taken = {a.rid for a in adm}
-                waiting = [r for r in waiting if r not in taken]
-                rnd = RoundLog(p_idx, adm, np.zeros((ph.n_decode, len(adm)), np.int32),
-                               np.zeros(len(adm), np.int64))
-                self._round(rnd, ph)
-                log.rounds.append(rnd)
+        for p_idx, ph in enumerate(self.w.phases):
+            self.run_phase(p_idx, ph, list(ph.rids), log)
         log.free_list = self.pool.free_list()
         log.stats = self.tree.stats()
         return log
+
+    def run_phase(self, p_idx, ph, rids, log: EpisodeLog) -> None:
+        """Serve the requests `rids` of phase `ph` in rounds (order, admit up to the batch
+        limit, extend, decode, finish), appending each round to `log`."""
+        w = self.w
+        waiting = list(rids)
+        while waiting:
+            order = self.tree.sched_order([w.requests[r].tokens for r in waiting], ph.policy)
+            waiting = [waiting[i] for i in order]
+            cand = waiting[:ph.batch_limit]
+            k, rows, pl, nodes = self.tree.admit_batch([w.requests[r].tokens for r in cand],
+                                                       ph.batch_limit, self.row_stride)
+            adm: List[Admission] = [
+                Admission(rid, int(pl[i]), len(w.requests[rid].tokens),
+                          rows[i, :len(w.requests[rid].tokens)].copy(), int(nodes[i]))
+                for i, rid in enumerate(cand[:k])]
+            if not adm:
+                raise RuntimeError(f"request {waiting[0]} cannot be admitted into an idle pool")
+            taken = {a.rid for a in adm}
+            waiting = [r for r in waiting if r not in taken]
+            rnd = RoundLog(p_idx, adm, np.zeros((ph.n_decode, len(adm)), np.int32),
+                           np.zeros(len(adm), np.int64))
+            self._round(rnd, ph)
+            log.rounds.append(rnd)
 
     def _round(self, rnd: RoundLog, ph):
         w = self.w
