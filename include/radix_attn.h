@@ -404,6 +404,29 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
                                int32_t num_splits, void *out, float *lse_out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc): radix_attn_decode with the same
+ * arguments and results, but no workspace argument. Its partial results and merge
+ * counters live in a device array built into the library, one per GPU, of
+ * radix_attn_decode_noalloc_max_bytes() bytes (64 MiB), held by each GPU the library
+ * runs on until the process ends. A call whose workspace would exceed that size
+ * (radix_attn_decode_workspace_size) returns RADIX_E_INVAL and launches nothing.
+ * Allocates nothing: the first call on a device looks up that device's array and
+ * clears its counters with a fill kernel on `stream`; every call leaves them clear.
+ * All calls on one GPU share its array, so calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. The stream's
+ * device must be the current device. */
+radix_status radix_attn_decode_noalloc(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                                       const void *q, const void *k_new, const void *v_new,
+                                       const float *scale_new, const int32_t *new_slots,
+                                       int32_t *req_to_token, int32_t rtt_stride,
+                                       const int32_t *req_rows, const int32_t *seq_lens,
+                                       int32_t batch, int32_t max_seq_len,
+                                       const radix_decode_plan *plan, int32_t num_splits,
+                                       void *out, float *lse_out, void *stream);
+/* Size in bytes of the built-in scratch array of radix_attn_decode_noalloc. */
+size_t radix_attn_decode_noalloc_max_bytes(void);
+
 /* ======================================================================
  * Kernel timing for measurement tools. While enabled, every kernel the
  * attention calls launch is bracketed by two HIP events recorded on the

@@ -117,6 +117,11 @@ _SIGS = {
                                     _vp, _vp, C.c_int32, _vp, _vp, C.c_int32, C.c_int32,
                                     C.POINTER(DecodePlan), C.c_int32, _vp, _vp, _vp, C.c_size_t,
                                     _vp]),
+    "radix_attn_decode_noalloc": (C.c_int, [C.POINTER(AttnShape), C.POINTER(KVBuffers), _vp, _vp,
+                                            _vp, _vp, _vp, _vp, C.c_int32, _vp, _vp, C.c_int32,
+                                            C.c_int32, C.POINTER(DecodePlan), C.c_int32, _vp, _vp,
+                                            _vp]),
+    "radix_attn_decode_noalloc_max_bytes": (C.c_size_t, []),
 }
 
 _LIB = None
@@ -514,6 +519,20 @@ def attn_decode(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token, 
         _ptr(new_slots), _ptr(req_to_token), int(req_to_token.shape[1]), _ptr(req_rows),
         _ptr(seq_lens), int(batch), int(max_seq_len), None if plan is None else C.byref(plan),
         int(num_splits), _ptr(out), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def attn_decode_noalloc(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token, req_rows,
+                        seq_lens, batch, max_seq_len, plan, num_splits, out, lse_out, stream=None):
+    """radix_attn_decode without a workspace (the library's built-in scratch array)."""
+    _check(load().radix_attn_decode_noalloc(
+        C.byref(shape), C.byref(kv), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(scale_new),
+        _ptr(new_slots), _ptr(req_to_token), int(req_to_token.shape[1]), _ptr(req_rows),
+        _ptr(seq_lens), int(batch), int(max_seq_len), None if plan is None else C.byref(plan),
+        int(num_splits), _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(load().radix_attn_decode_noalloc_max_bytes())
 
 
 # ---------------------------------------------------------------------- timing

@@ -2,6 +2,7 @@
 // kernel launches on the caller's stream. Nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -249,6 +250,51 @@ size_t partials_bytes(const radix_attn_shape *shape, int32_t batch, size_t parts
   const size_t b = static_cast<size_t>(batch) * shape->num_q_heads * parts *
                    (static_cast<size_t>(shape->head_dim_v) + 1) * sizeof(float);
   return (b + 255) / 256 * 256;
+}
+
+// ---------------------------------------------------------------- no-allocation decode
+// Scratch of radix_attn_decode_noalloc: a device array of the library itself, so that
+// callers that cannot allocate device memory (code under graph capture, serving loops
+// that forbid it) need no workspace. Each device holds its own copy for the life of the
+// process. In host code `scratch` names a host-side stand-in; the kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void zero_words_kernel(uint32_t *p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch. The first call on a device looks it up and
+// clears the merge-counter region with a fill kernel on `s` (ordered before the call's
+// decode launch); the decode kernels leave that region zero after every call.
+radix_status scratch_for_current_device(hipStream_t s, void **out) {
+  int dev = 0;
+  radix_status st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != RADIX_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device index above the scratch table");
+    return RADIX_E_INVAL;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != RADIX_OK) return st;
+    const int64_t words = static_cast<int64_t>(kMergeCounterBytes / sizeof(uint32_t));
+    zero_words_kernel<<<dim3(64), dim3(256), 0, s>>>(static_cast<uint32_t *>(p), words);
+    st = hip_status(hipGetLastError(), "scratch clear launch");
+    if (st != RADIX_OK) return st;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RADIX_OK;
 }
 
 }  // namespace
@@ -533,6 +579,36 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   Timed t(K_COMBINE, s);
   return hip_status(radix_launch::combine(false, a, batch, shape->head_dim_v, s), "combine launch");
 }
+
+radix_status radix_attn_decode_noalloc(const radix_attn_shape *shape, const radix_kv_buffers *kv,
+                                       const void *q, const void *k_new, const void *v_new,
+                                       const float *scale_new, const int32_t *new_slots,
+                                       int32_t *req_to_token, int32_t rtt_stride,
+                                       const int32_t *req_rows, const int32_t *seq_lens,
+                                       int32_t batch, int32_t max_seq_len,
+                                       const radix_decode_plan *plan, int32_t num_splits,
+                                       void *out, float *lse_out, void *stream) {
+  if (radix_attn_supported(shape, 1) != RADIX_OK) return RADIX_E_UNSUPPORTED;
+  REQUIRE(batch >= 0 && max_seq_len >= 0 && num_splits >= 0, "negative sizes");
+  if (batch == 0) return RADIX_OK;
+  size_t need = 0;
+  radix_status st = radix_attn_decode_workspace_size(shape, batch, max_seq_len, plan, num_splits,
+                                                     &need);
+  if (st != RADIX_OK) return st;
+  if (need > kScratchBytes) {
+    set_error("decode needs " + std::to_string(need) + " bytes of scratch, more than the " +
+              std::to_string(kScratchBytes) + " built into the library");
+    return RADIX_E_INVAL;
+  }
+  void *ws = nullptr;
+  st = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+  if (st != RADIX_OK) return st;
+  return radix_attn_decode(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token,
+                           rtt_stride, req_rows, seq_lens, batch, max_seq_len, plan, num_splits,
+                           out, lse_out, ws, kScratchBytes, stream);
+}
+
+size_t radix_attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 radix_status radix_profile_enable(int32_t capacity) {
   REQUIRE(capacity >= 0, "negative profiling capacity");

@@ -128,7 +128,7 @@ class Engine:
     def __init__(self, workload, device=None, use_plan: bool = True, num_splits: int = 0,
                  on_extend: Optional[Callable] = None, on_decode: Optional[Callable] = None,
                  min_members: int = 2, host_slots: bool = False,
-                 split_keys: Optional[int] = None):
+                 split_keys: Optional[int] = None, noalloc: bool = False):
         self.w = workload
         self.pool = _lib.KVPool(workload.pool_slots)
         self.tree = _lib.RadixTree(self.pool)
@@ -140,6 +140,7 @@ class Engine:
         self.min_members = min_members
         self.split_keys = split_keys
         self.host_slots = host_slots   # decode reads new slots from pinned host memory
+        self.noalloc = noalloc         # decode through the entry point without a workspace
         self._ws = None
         self.content = np.full(workload.pool_slots, -1, np.int64)   # harness bookkeeping
         self.row_stride = max(len(r.tokens) + len(r.out_tokens) for r in workload.requests)
@@ -295,11 +296,12 @@ class Engine:
         sc_new = None if d.sc_tab is None else d.sc_tab[rows]
         plan, _keep = self._plan_dev
         splits = self.num_splits or 0
-        ws_bytes = _lib.decode_workspace_size(d.shape, B, int(seq.max()), plan, splits)
-        # one workspace for every call (grown when a round needs more): the bf16 merge
-        # counters are zeroed once, at allocation, and every call leaves them zero
-        if self._ws is None or self._ws.numel() * 4 < ws_bytes:
-            self._ws = torch.zeros(max(ws_bytes // 4, 1), dtype=torch.float32, device=d.device)
+        if not self.noalloc:
+            ws_bytes = _lib.decode_workspace_size(d.shape, B, int(seq.max()), plan, splits)
+            # one workspace for every call (grown when a round needs more): the bf16 merge
+            # counters are zeroed once, at allocation, and every call leaves them zero
+            if self._ws is None or self._ws.numel() * 4 < ws_bytes:
+                self._ws = torch.zeros(max(ws_bytes // 4, 1), dtype=torch.float32, device=d.device)
         ws = self._ws
         out = torch.empty((B, s.num_q_heads, s.head_dim_v), dtype=d.q_dtype, device=d.device)
         lse = torch.empty((B, s.num_q_heads), dtype=torch.float32, device=d.device)
@@ -307,8 +309,12 @@ class Engine:
             new_slots = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).pin_memory()
         else:
             new_slots = d.i32(slots)
-        _lib.attn_decode(d.shape, d.kv, q, k_new, v_new, sc_new, new_slots, d.rtt, None,
-                         d.i32(seq), B, int(seq.max()), plan, splits, out, lse, ws)
+        if self.noalloc:
+            _lib.attn_decode_noalloc(d.shape, d.kv, q, k_new, v_new, sc_new, new_slots, d.rtt,
+                                     None, d.i32(seq), B, int(seq.max()), plan, splits, out, lse)
+        else:
+            _lib.attn_decode(d.shape, d.kv, q, k_new, v_new, sc_new, new_slots, d.rtt, None,
+                             d.i32(seq), B, int(seq.max()), plan, splits, out, lse, ws)
         if self.host_slots:
             torch.cuda.current_stream().synchronize()   # the pinned slots are read by the kernel
         if self.on_decode:
