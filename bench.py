@@ -45,12 +45,22 @@ def parse():
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", default="4",
                    help="4 (default: agent branching, the largest single-GPU workload), "
-                        "1, 2, 3A, 3B, 5bf16, 5fp8")
+                        "1, 2, 2fp8, 3A, 3B, 4fp8, 5bf16, 5fp8")
     p.add_argument("--no-plan", action="store_true", help="decode without shared segments")
     p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--min-members", type=int, default=2,
+                   help="members a shared segment needs to be read once for all of them")
     p.add_argument("--layers", type=int, default=4,
                    help="attention layers per step, each with its own K/V pool (same contents): "
                         "together they exceed the 256 MB last-level cache, as a model's layers do")
+    p.add_argument("--schedule", choices=["overlap", "sync", "free"], default="overlap",
+                   help="overlap: the host prepares decode step s+1 while earlier steps run, "
+                        "waiting only for step s+1-ahead; sync: it waits for each step before "
+                        "the next; free: it never waits inside a round")
+    p.add_argument("--ahead", type=int, default=1,
+                   help="overlap: decode steps the host may run ahead of the GPU")
+    p.add_argument("--no-kernel-timing", action="store_true",
+                   help="skip the second, kernel-timed pass (for external profilers)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -60,8 +70,8 @@ def parse():
 
 def workload_of(name):
     from workloads import config
-    table = {"1": (1, ""), "2": (2, ""), "3A": (3, "A"), "3B": (3, "B"), "4": (4, ""),
-             "5bf16": (5, "bf16"), "5fp8": (5, "fp8")}
+    table = {"1": (1, ""), "2": (2, ""), "2fp8": (2, "fp8"), "3A": (3, "A"), "3B": (3, "B"),
+             "4": (4, ""), "4fp8": (4, "fp8"), "5bf16": (5, "bf16"), "5fp8": (5, "fp8")}
     n, v = table[name]
     return config(n, v)
 
@@ -69,14 +79,22 @@ def workload_of(name):
 class Episode:
     """Pre-staged device inputs for every round of a workload, and one timed pass."""
 
-    def __init__(self, w, use_plan, splits, layers=1):
+    def __init__(self, w, use_plan, splits, layers=1, schedule="overlap", ahead=1,
+                 min_members=2):
         import torch
         from prefix_shared_kv_radix_amd import _lib
         from prefix_shared_kv_radix_amd.runner import DeviceState, Engine, build_decode_plan
         self.torch, self._lib, self.build_plan = torch, _lib, build_decode_plan
         self.w, self.use_plan, self.splits = w, use_plan, splits
+        self.min_members = min_members
+        # "overlap": the host prepares decode step s+1 (slot allocation, pinned slot rows,
+        # launches) while step s runs, and waits only for step s-1 (whose outputs a server
+        # would read); "sync": the host waits for every step before preparing the next
+        self.schedule = schedule
+        self.ahead = max(1, int(ahead))
+        self.step_evt = [_lib.Fence() for _ in range(self.ahead + 1)]
         # host-only pass: the rounds (and their plans) are deterministic
-        dry = Engine(w).run()
+        dry = Engine(w, min_members=min_members).run()
         self.rounds = dry.rounds
         dev = "cuda"
         max_batch = max(len(r.admissions) for r in dry.rounds)
@@ -166,7 +184,8 @@ class Episode:
                 raise RuntimeError("episode diverged from its dry run")
             plan_dev, keep = (None, [])
             if ph.n_decode and self.use_plan and B > 1:
-                plan_dev, keep = _lib.device_plan(self.build_plan(tree, nodes, 2), d.device)
+                plan_dev, keep = _lib.device_plan(self.build_plan(tree, nodes, self.min_members),
+                                                  d.device)
             if ph.extend != "host":
                 rtt_pin[:B].copy_(torch.from_numpy(rows))
                 d.rtt[:B].copy_(rtt_pin[:B], non_blocking=True)
@@ -210,6 +229,16 @@ class Episode:
                                          None if st["dsc"] is None else st["dsc"][s], slot_arg,
                                          d.rtt, None, st["seq_dev"][s], B, st["seq_max"][s],
                                          plan_dev, self.splits, st["dout"], None, self.ws, stream)
+                    if self.schedule == "free":
+                        continue
+                    k = len(self.step_evt)
+                    self.step_evt[s % k].record(stream)
+                    if self.schedule == "sync":
+                        self.step_evt[s % k].wait()
+                    elif s >= self.ahead:
+                        # step s - ahead has finished (a server reads its outputs now) while
+                        # the steps after it run
+                        self.step_evt[(s - self.ahead) % k].wait()
             if mark:
                 marks.append(("round_end", torch.cuda.Event(enable_timing=True)))
                 marks[-1][1].record()
@@ -442,7 +471,8 @@ def main():
     if args.layers < 1:
         print("--layers must be at least 1", file=sys.stderr)
         sys.exit(2)
-    ep = Episode(w, not args.no_plan, args.splits, args.layers)
+    ep = Episode(w, not args.no_plan, args.splits, args.layers, args.schedule, args.ahead,
+                 args.min_members)
     torch.cuda.synchronize()
     print(f"[bench] staged {w.name}: {len(ep.rounds)} rounds", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -460,14 +490,16 @@ def main():
     # the same K steps again with a HIP event pair around every launch (per-kernel
     # durations for the roofline); kept out of the region above because the per-launch
     # events cost the step several percent
-    _lib.profile_enable(1 << 17)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ep.run()
-    torch.cuda.synchronize()
-    prof = _lib.profile_read(1 << 17)
-    _lib.profile_enable(0)
-    print(f"[bench] kernel-timed {args.steps} more steps", file=sys.stderr, flush=True)
+    prof = []
+    if not args.no_kernel_timing:
+        _lib.profile_enable(1 << 17)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ep.run()
+        torch.cuda.synchronize()
+        prof = _lib.profile_read(1 << 17)
+        _lib.profile_enable(0)
+        print(f"[bench] kernel-timed {args.steps} more steps", file=sys.stderr, flush=True)
 
     # every figure below is per attention layer: an episode runs `layers` of them
     L = args.layers
@@ -489,6 +521,14 @@ def main():
     kernels = {n: {"launches": c // (args.steps * L), "ms_per_step": t / (args.steps * L),
                    "avg_us": 1e3 * t / c}
                for n, (c, t) in kern.items()}
+    if not kern:   # no kernel-timed pass: phase times only
+        out = {"metric": "decode tokens/s + achieved HBM GB/s (% peak), prefix-shared KV attention",
+               "value": dec_tokens / (ms_per_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+               "extend_ms_per_step": ext_ms, "decode_ms_per_step": dec_ms,
+               "config": {"workload": w.name, "layers": L, "schedule": args.schedule}}
+        print(json.dumps(out))
+        return
     dom = max(kern, key=lambda n: kern[n][1])
     byt, flop = algorithmic(w, ep, dom)
     t_dom = kern[dom][1] / (args.steps * L) / 1e3    # seconds per layer-episode in that kernel
@@ -528,7 +568,8 @@ def main():
                    "q_heads": w.shape.num_q_heads, "kv_heads": w.shape.num_kv_heads,
                    "head_dim": w.shape.head_dim_qk, "decode_tokens_per_step": dec_tokens,
                    "extend_tokens_per_step": ext_tokens, "shared_segments": not args.no_plan,
-                   "layers": L},
+                   "layers": L, "schedule": args.schedule,
+                   "ahead": args.ahead if args.schedule == "overlap" else None},
         "extend_ms_per_step": ext_ms,
         "decode_ms_per_step": dec_ms,
         "decode_only_tokens_per_s": dec_tokens / (dec_ms / 1e3) if dec_ms else None,

@@ -303,7 +303,8 @@ typedef struct {
 
 /* Shapes compiled into this library (anything else: RADIX_E_UNSUPPORTED):
  *   q F32, kv F32,  Dqk = Dv = 64,   Hq/Hkv in {1, 2, 4, 8}      (extend, decode)
- *   q BF16, kv BF16, Dqk = Dv = 128, Hq/Hkv in {1, 2, 4, 8}      (extend, decode)
+ *   q BF16, kv BF16 or FP8_E4M3, Dqk = Dv = 128, Hq/Hkv in {1, 2, 4, 8}
+ *       (extend, decode; fp8: one scale per token for its K and V rows)
  *   q BF16, kv BF16 or FP8_E4M3, Dqk = 576, Dv = 512, Hkv = 1,
  *       Hq = 128, v_is_k_prefix = 1                              (decode, store)  */
 radix_status radix_attn_supported(const radix_attn_shape *shape, int is_decode);
@@ -426,6 +427,22 @@ radix_status radix_attn_decode_noalloc(const radix_attn_shape *shape, const radi
                                        void *out, float *lse_out, void *stream);
 /* Size in bytes of the built-in scratch array of radix_attn_decode_noalloc. */
 size_t radix_attn_decode_noalloc_max_bytes(void);
+
+/* ======================================================================
+ * Step fences for a scheduler that runs one batch ahead of the GPU (SGLang
+ * feature article, §二: the host prepares the next batch's metadata while the
+ * GPU runs the current one, so the GPU never waits for the scheduler). A fence
+ * marks a point in a stream; waiting on it blocks the host until the work
+ * enqueued before it has finished. Unlike a default HIP event it makes device
+ * writes visible at device scope only (no system-scope cache writeback between
+ * steps): read device results on the host through a copy, not through mapped
+ * memory. Errors: E_INVAL on a NULL fence, E_HIP from the runtime.
+ * ====================================================================== */
+typedef struct radix_fence radix_fence;
+radix_status radix_fence_create(radix_fence **out);
+radix_status radix_fence_record(radix_fence *fence, void *stream);
+radix_status radix_fence_wait(radix_fence *fence);
+void radix_fence_destroy(radix_fence *fence);
 
 /* ======================================================================
  * Kernel timing for measurement tools. While enabled, every kernel the

@@ -19,7 +19,8 @@ dims of the row, the output reads its first 512 dims.
 
 Storage decoding: bf16 is the upper half of an IEEE binary32; fp8 E4M3 (OCP
 'fn': bias 7, no infinities, S.1111.111 = NaN, max 448) times the token's
-fp32 scale.
+fp32 scale (KV Cache FP8, SGLang feature article §一; one scale per token,
+shared by the token's K and V rows of every KV head where V is stored apart).
 """
 from __future__ import annotations
 
@@ -103,6 +104,8 @@ def request_kv(workload, kv_ids, dtype=np.float64):
         k = decode_storage(k_tab[rows], s.kv_dtype, None, dtype)
     if s.v_is_k_prefix:
         v = k[:, :, :s.head_dim_v]
+    elif s.kv_dtype == "fp8":   # the token's one scale serves its K and V rows
+        v = decode_storage(v_tab[rows], "fp8", k_scale[rows], dtype)
     else:
         v = decode_storage(v_tab[rows], s.kv_dtype, None, dtype)
     return k, v

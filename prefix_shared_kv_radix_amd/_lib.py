@@ -99,6 +99,10 @@ _SIGS = {
                                         _i64p, _i64p, _i64p]),
     "radix_req_finish_batch": (C.c_int, [_vp, _i32p, _i64p, _i32p, C.c_int64, _i64p, _i64p,
                                          C.c_int64, _i64p]),
+    "radix_fence_create": (C.c_int, [C.POINTER(_vp)]),
+    "radix_fence_record": (C.c_int, [_vp, _vp]),
+    "radix_fence_wait": (C.c_int, [_vp]),
+    "radix_fence_destroy": (None, [_vp]),
     "radix_profile_enable": (C.c_int, [C.c_int32]),
     "radix_profile_read": (C.c_int, [_i32p, C.POINTER(C.c_float), C.c_int32, _i32p]),
     "radix_kernel_name": (C.c_char_p, [C.c_int32]),
@@ -533,6 +537,28 @@ def attn_decode_noalloc(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to
 
 def decode_noalloc_max_bytes() -> int:
     return int(load().radix_attn_decode_noalloc_max_bytes())
+
+
+class Fence:
+    """A point in a stream the host can wait for (device-scope release only)."""
+
+    def __init__(self):
+        h = _vp()
+        _check(load().radix_fence_create(C.byref(h)))
+        self.h = h
+
+    def record(self, stream=None):
+        _check(load().radix_fence_record(self.h, _stream(stream)))
+
+    def wait(self):
+        _check(load().radix_fence_wait(self.h))
+
+    def close(self):
+        if self.h and not sys.is_finalizing():
+            load().radix_fence_destroy(self.h)
+        self.h = None
+
+    __del__ = close
 
 
 # ---------------------------------------------------------------------- timing

@@ -71,6 +71,9 @@ struct AttnArgs {
   const void *k_new, *v_new;
   const int32_t *new_slots;
   int32_t *rtt_mut;
+  // fp8 K/V: one fp32 scale per slot (K and V rows of every KV head) and the new token's
+  float *kv_scale;
+  const float *scale_new;
   void *out;
   float *lse;
   float *ws_o, *ws_lse;
@@ -105,15 +108,18 @@ hipError_t mla(const MlaArgs &a, hipStream_t s);
 // 2: shared segment -> partial, 3: decode private tail -> final output (merges shared partials)
 hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, unsigned splits,
                 hipStream_t s);
-// extend attention with bf16 MFMA tiles (128 query rows x 64-key tiles)
-hipError_t mfma(int G, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s);
+// extend attention with bf16 MFMA tiles (128 query rows x 64-key tiles); fp8: K/V bytes
+// times their slot's scale, rounded to bf16 as the tiles are staged
+hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s);
 // bf16 decode over the private keys of each request (split into `splits` chunks): output
-// written directly, or partials merged in-kernel by the last producer (merge_cnt)
-hipError_t decode_tail_bf16(int G, const AttnArgs &a, unsigned batch, unsigned splits, hipStream_t s);
+// written directly, or partials merged in-kernel by the last producer (merge_cnt); fp8 K/V
+// rows are converted exactly and their scale applied to the score and the probability
+hipError_t decode_tail_bf16(int G, bool fp8, const AttnArgs &a, unsigned batch, unsigned splits,
+                            hipStream_t s);
 hipError_t combine(bool bf16, const AttnArgs &a, int batch, int Dv, hipStream_t s);
 // one launch: shared-segment MFMA tiles + private-tail waves; the last producer of each
 // (request, KV head) merges its partials (merge_cnt)
-hipError_t decode_fused(int G, const AttnArgs &a, int max_rows, unsigned seg_items,
+hipError_t decode_fused(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned seg_items,
                         unsigned n_items, unsigned nsplit, hipStream_t s);
 
 }  // namespace radix_launch

@@ -26,7 +26,7 @@ constexpr float kLog2e = 1.4426950408889634f;
     }                      \
   } while (0)
 
-enum class Kind { None, GqaF32, GqaBf16, MlaBf16, MlaFp8 };
+enum class Kind { None, GqaF32, GqaBf16, GqaFp8, MlaBf16, MlaFp8 };
 
 Kind classify(const radix_attn_shape *s) {
   if (!s || s->num_kv_heads <= 0 || s->num_q_heads <= 0 || s->num_q_heads % s->num_kv_heads)
@@ -40,6 +40,9 @@ Kind classify(const radix_attn_shape *s) {
     if (s->q_dtype == RADIX_BF16 && s->kv_dtype == RADIX_BF16 && s->head_dim_qk == 128 &&
         s->head_dim_v == 128)
       return Kind::GqaBf16;
+    if (s->q_dtype == RADIX_BF16 && s->kv_dtype == RADIX_FP8_E4M3 && s->head_dim_qk == 128 &&
+        s->head_dim_v == 128)
+      return Kind::GqaFp8;
   }
   if (s->v_is_k_prefix && s->num_kv_heads == 1 && s->num_q_heads == 128 && s->head_dim_qk == 576 &&
       s->head_dim_v == 512 && s->q_dtype == RADIX_BF16) {
@@ -50,6 +53,9 @@ Kind classify(const radix_attn_shape *s) {
 }
 
 int elem_bytes(int dtype) { return dtype == RADIX_F32 ? 4 : dtype == RADIX_BF16 ? 2 : 1; }
+
+// GQA with bf16 queries (bf16 or fp8 K/V): matrix-core tiles, in-kernel merge
+bool gqa_mfma(Kind k) { return k == Kind::GqaBf16 || k == Kind::GqaFp8; }
 
 radix_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return RADIX_OK;
@@ -96,6 +102,7 @@ AttnArgs attn_args(const radix_attn_shape *s, const radix_kv_buffers *kv, const 
   a.scale_log2 = s->sm_scale * kLog2e;
   a.num_splits = 1;
   a.whole_reqs = 0;
+  a.kv_scale = kv->kv_scale;
   return a;
 }
 
@@ -214,7 +221,7 @@ TailCut tail_cut(const radix_attn_shape *shape, int batch, int max_seq_len,
   if (num_splits > 0) return {num_splits, num_splits == 1 ? batch : 0};
   const int plen = private_len_bound(max_seq_len, plan);
   const int s = auto_splits(batch, shape->num_kv_heads, plen);
-  const bool fused = plan && plan->num_segments > 0 && classify(shape) == Kind::GqaBf16;
+  const bool fused = plan && plan->num_segments > 0 && gqa_mfma(classify(shape));
   const int late = batch * RADIX_FUSED_LATE_PCT / 100;
   if (s > 1 || !fused || late == 0 || RADIX_FUSED_LATE_SPLITS < 2 ||
       plen < 32 * RADIX_FUSED_LATE_SPLITS)
@@ -379,6 +386,7 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
           "missing extend argument");
   REQUIRE(max_extend <= total_extend, "max_extend exceeds total_extend");
   REQUIRE(!k_new || shape->v_is_k_prefix || v_new, "missing new V rows");
+  REQUIRE(!k_new || shape->kv_dtype != RADIX_FP8_E4M3 || scale_new, "missing new fp8 scales");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (k_new) {
     StoreArgs sa = store_args(shape, kv, k_new, v_new, scale_new);
@@ -400,9 +408,11 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
   a.batch = batch;
   a.num_splits = 1;
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  if (classify(shape) == Kind::GqaBf16) {
+  const Kind kind = classify(shape);
+  if (gqa_mfma(kind)) {
     Timed t(K_EXTEND_MFMA, s);
-    return hip_status(radix_launch::mfma(G, a, max_extend * G, batch, s), "extend launch");
+    return hip_status(radix_launch::mfma(G, kind == Kind::GqaFp8, a, max_extend * G, batch, s),
+                      "extend launch");
   }
   Timed t(K_EXTEND_VALU, s);
   return hip_status(radix_launch::valu(false, G, 1, a, total_extend, 1, s), "extend launch");
@@ -502,12 +512,12 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   const bool direct = !use_plan && splits == 1;
   size_t need = 0;
   radix_attn_decode_workspace_size(shape, batch, max_seq_len, plan, splits, &need);
-  REQUIRE((direct && kind != Kind::GqaBf16) || (workspace && workspace_bytes >= need),
+  REQUIRE((direct && !gqa_mfma(kind)) || (workspace && workspace_bytes >= need),
           "decode workspace too small");
-  REQUIRE(direct || kind != Kind::GqaBf16 ||
+  REQUIRE(direct || !gqa_mfma(kind) ||
               static_cast<int64_t>(batch) * shape->num_kv_heads <= kMergeCounters,
           "batch * num_kv_heads above the merge counter capacity (65024)");
-  char *ws_parts = static_cast<char *>(workspace) + (kind == Kind::GqaBf16 ? kMergeCounterBytes : 0);
+  char *ws_parts = static_cast<char *>(workspace) + (gqa_mfma(kind) ? kMergeCounterBytes : 0);
   float *ws_o = direct ? nullptr : reinterpret_cast<float *>(ws_parts);
   float *ws_lse = direct ? nullptr
                          : ws_o + static_cast<size_t>(batch) * shape->num_q_heads * parts *
@@ -529,7 +539,9 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
   a.v_new = v_new;
   a.new_slots = new_slots;
   a.rtt_mut = req_to_token;
-  const bool bf16 = kind == Kind::GqaBf16;
+  a.scale_new = scale_new;
+  const bool bf16 = gqa_mfma(kind);
+  const bool fp8 = kind == Kind::GqaFp8;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (use_plan) {
     a.seg_row = plan->seg_row;
@@ -552,11 +564,11 @@ radix_status radix_attn_decode(const radix_attn_shape *shape, const radix_kv_buf
     Timed t(use_plan ? K_DECODE_FUSED : K_DECODE_TAIL, s);
     if (use_plan)
       return hip_status(radix_launch::decode_fused(
-                            G, a, plan->max_members * G,
+                            G, fp8, a, plan->max_members * G,
                             static_cast<unsigned>(plan->num_seg_items),
                             static_cast<unsigned>(batch), static_cast<unsigned>(splits), s),
                         "decode launch");
-    return hip_status(radix_launch::decode_tail_bf16(G, a, static_cast<unsigned>(batch),
+    return hip_status(radix_launch::decode_tail_bf16(G, fp8, a, static_cast<unsigned>(batch),
                                                      static_cast<unsigned>(splits), s),
                       "decode launch");
   }
@@ -609,6 +621,33 @@ radix_status radix_attn_decode_noalloc(const radix_attn_shape *shape, const radi
 }
 
 size_t radix_attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+radix_status radix_fence_create(radix_fence **out) {
+  REQUIRE(out, "null output pointer");
+  hipEvent_t e = nullptr;
+  radix_status st = hip_status(
+      hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence),
+      "hipEventCreateWithFlags");
+  if (st != RADIX_OK) return st;
+  *out = reinterpret_cast<radix_fence *>(e);
+  return RADIX_OK;
+}
+
+radix_status radix_fence_record(radix_fence *fence, void *stream) {
+  REQUIRE(fence, "null fence");
+  return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(fence),
+                                   static_cast<hipStream_t>(stream)),
+                    "hipEventRecord");
+}
+
+radix_status radix_fence_wait(radix_fence *fence) {
+  REQUIRE(fence, "null fence");
+  return hip_status(hipEventSynchronize(reinterpret_cast<hipEvent_t>(fence)), "hipEventSynchronize");
+}
+
+void radix_fence_destroy(radix_fence *fence) {
+  if (fence) (void)hipEventDestroy(reinterpret_cast<hipEvent_t>(fence));
+}
 
 radix_status radix_profile_enable(int32_t capacity) {
   REQUIRE(capacity >= 0, "negative profiling capacity");

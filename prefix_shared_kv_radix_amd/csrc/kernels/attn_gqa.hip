@@ -516,16 +516,27 @@ __device__ __forceinline__ void merge_requests_bf16(const AttnArgs &a, const int
 #ifndef RADIX_TAIL_STAGES
 #define RADIX_TAIL_STAGES 3
 #endif
+#ifndef RADIX_TAIL_GROUP
+#define RADIX_TAIL_GROUP 1
+#endif
 
 __device__ __forceinline__ int32_t take_ticket(int32_t *q);
 
 // One private-tail item w = (request, split, KV head) on one wave. With a work queue
 // (queue != NULL) the wave draws its next ticket into `ticket` (lane 0) once its keys
 // are read, so the atomic's latency overlaps the rest of the item.
-template <int G>
+template <bool FP8> struct RowOf { typedef u32x4 type; };   // one lane's part of a row
+template <> struct RowOf<true> { typedef u32x2 type; };
+
+template <int G, bool FP8>
 __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_items, int nsplit,
                                                int32_t *queue = nullptr, int32_t *ticket = nullptr) {
   constexpr int D = 128;
+  // bf16 rows: 16 bytes per lane; fp8 rows: 8 bytes per lane (the same 8 dims), converted
+  // exactly to bf16 pairs, the row's scale applied to its score and probability
+  constexpr int EB = FP8 ? 1 : 2;
+  constexpr int LB = 8 * EB;
+  using RowT = typename RowOf<FP8>::type;
   constexpr int NB = RADIX_TAIL_STAGES;
   constexpr float kGrow = 8.f;
   int lane = threadIdx.x & 63;
@@ -542,9 +553,19 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   const bool one = w < whole * a.Hkv;
   const int wr = one ? w : w - whole * a.Hkv;
   const int ns_tail = one ? 1 : nsplit;   // private parts of this request
-  const int kvh = wr % a.Hkv;
+  int kvh = wr % a.Hkv;
   const int split = (wr / a.Hkv) % ns_tail;
-  const int b = (one ? 0 : whole) + wr / (a.Hkv * ns_tail);
+  int b = (one ? 0 : whole) + wr / (a.Hkv * ns_tail);
+  // Requests read whole are taken RADIX_TAIL_GROUP at a time per KV head: the waves of one
+  // block then read the same KV head of consecutive requests, which share their
+  // key prefix when consecutive requests branch off one tree node (the rows come once
+  // from HBM, then from the shared caches).
+  constexpr int TG = RADIX_TAIL_GROUP;
+  if (TG > 1 && one && w < (whole / TG) * TG * a.Hkv) {
+    const int r = w % (TG * a.Hkv);
+    kvh = r / TG;
+    b = (w / (TG * a.Hkv)) * TG + r % TG;
+  }
 
   const int hi = a.seq_lens[b];
   const int lo = a.private_start ? a.private_start[b] : 0;
@@ -555,20 +576,22 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   const int s_lo = lo + split * chunk;
   const int s_hi = min(hi, s_lo + chunk);
 
-  const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * D * 2;
-  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * D * 2 + sub * 16;
-  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * 2 + sub * 16;
+  const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * D * EB;
+  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * D * EB + sub * LB;
+  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * D * EB + sub * LB;
   const bool fuse_new = a.k_new != nullptr;
   const char *knew = nullptr, *vnew = nullptr;
   // the new token's slot: read now (new_slots may be pinned host memory), used at the end
   const bool store_new = fuse_new && split == 0;
   const int64_t new_at = static_cast<int64_t>(a.req_rows ? a.req_rows[b] : b) * a.rtt_stride + hi - 1;
   int32_t new_slot = 0;
+  float sc_new = 1.f;
   if (fuse_new) {
-    const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D * 2 + sub * 16;
+    const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D * EB + sub * LB;
     knew = reinterpret_cast<const char *>(a.k_new) + off;
     vnew = reinterpret_cast<const char *>(a.v_new) + off;
     if (store_new) new_slot = a.new_slots ? a.new_slots[b] : a.rtt[new_at];
+    if (FP8) sc_new = a.scale_new[b];
   }
   const int ns_b = a.req_num_parts ? a.req_num_parts[b] : 0;
   const int expected = ns_b + ns_tail;   // producers of this request's output
@@ -611,7 +634,10 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   // With 8 heads the kernel spills, and the compiler places the waits.
   constexpr bool kOwnWaits = G <= 4;
   static_assert(NB >= 3, "the slot wait covers the rows being computed only for NB >= 3");
-  u32x4 kbuf[NB][4], vbuf[NB][4];
+  // loads of one iteration's rows: K and V (and, fp8, the rows' scales) for 4 rows
+  constexpr int kRowLoads = FP8 ? 12 : 8;
+  RowT kbuf[NB][4], vbuf[NB][4];
+  float cbuf[NB][4];   // fp8: the rows' scales
   int32_t sbuf[NB][4];
   auto load_slots = [&](int base, int32_t *sl) {
 #pragma unroll
@@ -620,37 +646,66 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
       sl[k] = kOwnWaits ? ld_async4(p) : *p;
     }
   };
-  auto load_kv = [&](const int32_t *sl, u32x4 *kd, u32x4 *vd) {
+  auto load_kv = [&](const int32_t *sl, RowT *kd, RowT *vd, float *cd) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const char *kp = kb + static_cast<int64_t>(sl[k]) * row_bytes;
       const char *vp = vb + static_cast<int64_t>(sl[k]) * row_bytes;
-      kd[k] = kOwnWaits ? ld_async16<0>(kp) : ldg16(kp);
-      vd[k] = kOwnWaits ? ld_async16<0>(vp) : ldg16(vp);
+      if constexpr (FP8) {
+        kd[k] = kOwnWaits ? ld_async8(kp) : *reinterpret_cast<const u32x2 *>(kp);
+        vd[k] = kOwnWaits ? ld_async8(vp) : *reinterpret_cast<const u32x2 *>(vp);
+        cd[k] = kOwnWaits ? ld_async4f(a.kv_scale + sl[k]) : a.kv_scale[sl[k]];
+      } else {
+        kd[k] = kOwnWaits ? ld_async16<0>(kp) : ldg16(kp);
+        vd[k] = kOwnWaits ? ld_async16<0>(vp) : ldg16(vp);
+      }
     }
   };
   // wait until at most N loads are outstanding; sl and the rows of one ring stage are
   // tied to the wait so that no use of them is scheduled before it
-  auto wait_ring = [&](auto n, int32_t *sl, u32x4 *kd, u32x4 *vd) {
-    if constexpr (kOwnWaits)
+  auto wait_ring = [&](auto n, int32_t *sl, RowT *kd, RowT *vd, float *cd) {
+    if constexpr (kOwnWaits && FP8)
+      asm volatile("s_waitcnt vmcnt(%16)"
+                   : "+v"(sl[0]), "+v"(sl[1]), "+v"(sl[2]), "+v"(sl[3]), "+v"(kd[0]), "+v"(kd[1]),
+                     "+v"(kd[2]), "+v"(kd[3]), "+v"(vd[0]), "+v"(vd[1]), "+v"(vd[2]), "+v"(vd[3]),
+                     "+v"(cd[0]), "+v"(cd[1]), "+v"(cd[2]), "+v"(cd[3])
+                   : "n"(decltype(n)::value)
+                   : "memory");
+    else if constexpr (kOwnWaits)
       asm volatile("s_waitcnt vmcnt(%12)"
                    : "+v"(sl[0]), "+v"(sl[1]), "+v"(sl[2]), "+v"(sl[3]), "+v"(kd[0]), "+v"(kd[1]),
                      "+v"(kd[2]), "+v"(kd[3]), "+v"(vd[0]), "+v"(vd[1]), "+v"(vd[2]), "+v"(vd[3])
                    : "n"(decltype(n)::value)
                    : "memory");
   };
-  // rows k = 0..3 of this lane (row base + 4k + r4) with valid flags `vmask` bit k
-  auto compute = [&](int vmask, const u32x4 *kr, const u32x4 *vr) {
+  // a lane's 8 dims of a row as 4 packed bf16 pairs
+  auto words = [](const RowT &r, uint32_t (&w)[4]) {
+    if constexpr (FP8) {
+      w[0] = fp8x2_to_bf16x2<false>(r[0]);
+      w[1] = fp8x2_to_bf16x2<true>(r[0]);
+      w[2] = fp8x2_to_bf16x2<false>(r[1]);
+      w[3] = fp8x2_to_bf16x2<true>(r[1]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = r[c];
+    }
+  };
+  // rows k = 0..3 of this lane (row base + 4k + r4) with valid flags `vmask` bit k; cr:
+  // the rows' scales (fp8)
+  auto compute = [&](int vmask, const RowT *kr, const RowT *vr, const float *cr) {
     float s[4][G];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      uint32_t kw[4];
+      words(kr[k], kw);
+      const float sk = FP8 ? a.scale_log2 * cr[k] : a.scale_log2;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) d = dot2bf(qp[h][c], kr[k][c], d);
+        for (int c = 0; c < 4; ++c) d = dot2bf(qp[h][c], kw[c], d);
         d = sum16(d);
-        s[k][h] = ((vmask >> k) & 1) ? d * a.scale_log2 : -INFINITY;
+        s[k][h] = ((vmask >> k) & 1) ? d * sk : -INFINITY;
       }
     }
     bool grow = false;
@@ -675,15 +730,23 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
 #pragma unroll
       for (int k = 0; k < 4; ++k) p[k] = __builtin_amdgcn_exp2f(s[k][h] - m[h]);
       l[h] += (p[0] + p[1]) + (p[2] + p[3]);
-      pp[0][h] = pack2bf(p[0], p[1]);
-      pp[1][h] = pack2bf(p[2], p[3]);
+      if constexpr (FP8) {   // the value rows' scales go with their probabilities
+        pp[0][h] = pack2bf(p[0] * cr[0], p[1] * cr[1]);
+        pp[1][h] = pack2bf(p[2] * cr[2], p[3] * cr[3]);
+      } else {
+        pp[0][h] = pack2bf(p[0], p[1]);
+        pp[1][h] = pack2bf(p[2], p[3]);
+      }
     }
+    uint32_t vw[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) words(vr[k], vw[k]);
     // pair dim e of row 2i with dim e of row 2i+1
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const uint32_t a0 = vr[2 * i][c], a1 = vr[2 * i + 1][c];
+        const uint32_t a0 = vw[2 * i][c], a1 = vw[2 * i + 1][c];
         const uint32_t lo2 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // {row.lo, row'.lo}
         const uint32_t hi2 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // {row.hi, row'.hi}
 #pragma unroll
@@ -717,9 +780,12 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
 #pragma unroll
     for (int j = 1; j < NB; ++j) {
       load_slots(s_lo + 16 * j, sbuf[j]);
-      if (j == 1) wait_ring(std::integral_constant<int, 4>{}, sbuf[0], kbuf[0], vbuf[0]);
-      else wait_ring(std::integral_constant<int, 12>{}, sbuf[j - 1], kbuf[j - 1], vbuf[j - 1]);
-      load_kv(sbuf[j - 1], kbuf[j - 1], vbuf[j - 1]);
+      if (j == 1)
+        wait_ring(std::integral_constant<int, 4>{}, sbuf[0], kbuf[0], vbuf[0], cbuf[0]);
+      else
+        wait_ring(std::integral_constant<int, kRowLoads + 4>{}, sbuf[j - 1], kbuf[j - 1],
+                  vbuf[j - 1], cbuf[j - 1]);
+      load_kv(sbuf[j - 1], kbuf[j - 1], vbuf[j - 1], cbuf[j - 1]);
     }
     for (int base = s_lo; base < pool_hi; base += 16 * NB) {
 #pragma unroll
@@ -727,31 +793,35 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
         const int it = base + 16 * j;
         const int jl = (j + NB - 1) % NB;
         load_slots(it + 16 * NB, sbuf[j]);
-        // younger than the slots of iteration t+NB-1: the rows of t+NB-2 (8 loads) and
-        // the slots just issued (4); the rows of t are older, so they have landed
-        wait_ring(std::integral_constant<int, 12>{}, sbuf[jl], kbuf[j], vbuf[j]);
-        load_kv(sbuf[jl], kbuf[jl], vbuf[jl]);
+        // younger than the slots of iteration t+NB-1: the rows of t+NB-2 (kRowLoads loads)
+        // and the slots just issued (4); the rows of t are older, so they have landed
+        wait_ring(std::integral_constant<int, kRowLoads + 4>{}, sbuf[jl], kbuf[j], vbuf[j],
+                  cbuf[j]);
+        load_kv(sbuf[jl], kbuf[jl], vbuf[jl], cbuf[jl]);
         int vmask = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) vmask |= (it + 4 * k + r4 < pool_hi) << k;
-        compute(vmask, kbuf[j], vbuf[j]);
+        compute(vmask, kbuf[j], vbuf[j], cbuf[j]);
       }
     }
     // loads past the end are still in flight into the ring: let them land before the
     // ring's registers can be reused
 #pragma unroll
-    for (int j = 0; j < NB; ++j) wait_ring(std::integral_constant<int, 0>{}, sbuf[j], kbuf[j], vbuf[j]);
+    for (int j = 0; j < NB; ++j)
+      wait_ring(std::integral_constant<int, 0>{}, sbuf[j], kbuf[j], vbuf[j], cbuf[j]);
   }
   if (fuse_new && hi - 1 >= s_lo && hi - 1 < s_hi) {   // (uniform) the newest key
-    u32x4 kr[4], vr[4];
-    kr[0] = ldg16(knew);
-    vr[0] = ldg16(vnew);
+    RowT kr[4], vr[4];
+    float cr[4];
+    kr[0] = *reinterpret_cast<const RowT *>(knew);
+    vr[0] = *reinterpret_cast<const RowT *>(vnew);
 #pragma unroll
-    for (int k = 1; k < 4; ++k) {
+    for (int k = 0; k < 4; ++k) {
       kr[k] = kr[0];
       vr[k] = vr[0];
+      cr[k] = sc_new;
     }
-    compute(r4 == 0 ? 1 : 0, kr, vr);
+    compute(r4 == 0 ? 1 : 0, kr, vr, cr);
   }
 
   if (queue) *ticket = take_ticket(queue);
@@ -761,8 +831,9 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
     if (a.new_slots && kvh == 0 && sub == 0) a.rtt_mut[new_at] = new_slot;
     char *kd = const_cast<char *>(kb) + static_cast<int64_t>(new_slot) * row_bytes;
     char *vd = const_cast<char *>(vb) + static_cast<int64_t>(new_slot) * row_bytes;
-    *reinterpret_cast<u32x4 *>(kd) = ldg16(knew);
-    *reinterpret_cast<u32x4 *>(vd) = ldg16(vnew);
+    *reinterpret_cast<RowT *>(kd) = *reinterpret_cast<const RowT *>(knew);
+    *reinterpret_cast<RowT *>(vd) = *reinterpret_cast<const RowT *>(vnew);
+    if (FP8 && kvh == 0 && sub == 0) a.kv_scale[new_slot] = sc_new;
   }
   // merge counter of this (request, KV head), read now for the single-chunk fold below
   // so that its round trip overlaps the cross-lane reduction (a stale, lower count only
@@ -886,7 +957,7 @@ __device__ __forceinline__ int32_t take_ticket(int32_t *q) {
   return t;   // lane 0's value; read with readfirstlane where it is used
 }
 
-template <int G>
+template <int G, bool FP8>
 __global__ __launch_bounds__(256, G >= 8 ? 1 : 2) void tail_bf16_kernel(AttnArgs a, int n_items,
                                                                         int nsplit) {
   const int total = tail_items(min(a.whole_reqs, n_items), n_items, nsplit, a.Hkv);
@@ -902,7 +973,7 @@ __global__ __launch_bounds__(256, G >= 8 ? 1 : 2) void tail_bf16_kernel(AttnArgs
                    (nwaves - k + shards - 1) / shards - 1;
   while (w < total) {
     int32_t ticket = 0;
-    tail_bf16_body<G>(a, w, n_items, nsplit, queue, &ticket);
+    tail_bf16_body<G, FP8>(a, w, n_items, nsplit, queue, &ticket);
     if (!queue) break;
     const int t = __builtin_amdgcn_readfirstlane(ticket);
     if (t == last && (threadIdx.x & 63) == 0)
@@ -941,7 +1012,7 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
 // K/V tiles go global -> LDS with direct 16-byte loads, two stages: tile t+1 is in flight
 // while tile t is multiplied. Query rows are a request's new tokens x heads (extend,
 // causal) or the members of a shared radix segment x heads (decode partials).
-template <int G, bool SEG>
+template <int G, bool SEG, bool FP8>
 __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item, int kvh,
                                           uint8_t (*smem)[2][MF_TILE]) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1014,23 +1085,59 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   // loaders: wave w fills rows 16w .. 16w+15 of each tile, 4 rows per instruction;
   // lane i lands at byte 16*i of the instruction's 1 KB, i.e. row +i/16, physical chunk
   // i%16, so it fetches logical chunk (i%16) ^ mf_row_swz(row) of that row.
-  const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * MF_D * 2;
-  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * MF_D * 2;
-  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * MF_D * 2;
+  // fp8 K/V: rows of 128 bytes. Wave w stages its rows 16w .. 16w+15 raw, eight rows per
+  // direct load (lane i: row +i/8, 16-byte chunk i%8) into one linear staging tile, then
+  // converts those same chunks (times the row's scale, rounded to bf16) into the swizzled
+  // bf16 tile that the matrix code below reads; the bf16 tile is single-buffered (the next
+  // tile's raw bytes are in flight in the staging tile while it is used).
+  constexpr int EB = FP8 ? 1 : 2;
+  constexpr int NSL = FP8 ? 2 : 4;   // slot-list entries per lane per tile
+  const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * MF_D * EB;
+  const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * MF_D * EB;
+  const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * MF_D * EB;
+  uint8_t *stg = smem[1][0];   // fp8 staging: K rows 0..63 (8 KB), then V rows
   const int last = hi - 1;
-  int32_t sl[4];
+  int32_t sl[NSL];
+  float rsc[NSL];   // fp8: scales of the rows this lane stages
   auto load_slots = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sl[j] = rtt_row[min(kt + wave * 16 + 4 * j + (lane >> 4), last)];
+    for (int j = 0; j < NSL; ++j) {
+      const int r = FP8 ? wave * 16 + 8 * j + (lane >> 3) : wave * 16 + 4 * j + (lane >> 4);
+      sl[j] = rtt_row[min(kt + r, last)];
+    }
   };
   auto issue = [&](int stage) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wave * 16 + 4 * j + (lane >> 4);
-      const int c = (lane & 15) ^ mf_row_swz(r);
-      const int64_t off = static_cast<int64_t>(sl[j]) * row_bytes + c * 16;
-      lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
-      lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
+    for (int j = 0; j < NSL; ++j) {
+      if constexpr (FP8) {
+        const int64_t off = static_cast<int64_t>(sl[j]) * row_bytes + (lane & 7) * 16;
+        lds_load16(kb + off, stg + (wave * 16 + 8 * j) * 128);
+        lds_load16(vb + off, stg + 8192 + (wave * 16 + 8 * j) * 128);
+        rsc[j] = a.kv_scale[sl[j]];
+      } else {
+        const int r = wave * 16 + 4 * j + (lane >> 4);
+        const int c = (lane & 15) ^ mf_row_swz(r);
+        const int64_t off = static_cast<int64_t>(sl[j]) * row_bytes + c * 16;
+        lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
+        lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
+      }
+    }
+  };
+  // fp8: staged chunks of this lane -> bf16 tile (the caller has waited for the loads)
+  auto convert = [&]() {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int j = 0; j < NSL; ++j) {
+        const int r = wave * 16 + 8 * j + (lane >> 3), c = lane & 7;
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+          const u32x4 raw = *reinterpret_cast<const u32x4 *>(stg + kv * 8192 + r * 128 + c * 16);
+          u32x4 lo16, hi16;
+          fp8x16_to_bf16(raw, rsc[j], lo16, hi16);
+          *reinterpret_cast<u32x4 *>(&smem[0][kv][mf_swz(r, 2 * c)]) = lo16;
+          *reinterpret_cast<u32x4 *>(&smem[0][kv][mf_swz(r, 2 * c + 1)]) = hi16;
+        }
+      }
     }
   };
 
@@ -1041,20 +1148,30 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (FP8 && lo < hi) {
+    convert();
+    lds_barrier();
+  }
 
   for (int kt = lo, t = 0; kt < hi; kt += MF_BN, ++t) {
-    const int stage = t & 1;
-    if (kt + MF_BN < hi) {
+    const int stage = FP8 ? 0 : t & 1;
+    const bool more = kt + MF_BN < hi;
+    if (more) {
       issue(stage ^ 1);
       if (kt + 2 * MF_BN < hi) load_slots(kt + 2 * MF_BN);
     }
     const uint8_t *Kt = smem[stage][0];
     const uint8_t *Vt = smem[stage][1];
     // a wave whose 32 rows are all past the block's rows (small shared segments) only
-    // loads its share of each tile and keeps the barriers, leaving the SIMD to others
+    // loads (and, fp8, converts) its share of each tile and keeps the barriers, leaving
+    // the SIMD to others
     if (!wave_active) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (FP8 && more) {
+        convert();
+        lds_barrier();
+      }
       continue;
     }
 
@@ -1171,6 +1288,10 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (FP8 && more) {   // the next tile's bytes have landed and nobody reads this tile now
+      convert();
+      lds_barrier();
+    }
   }
 
   l_run += xor32(l_run);
@@ -1254,19 +1375,19 @@ __device__ __forceinline__ int xcd_logical(int bid, int nblocks) {
 }
 
 // extend: logical block -> (tile, request, kvh), tile fastest
-template <int G>
+template <int G, bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
   const int nblocks = tiles * items * a.Hkv;
   const int lb = xcd_logical(blockIdx.x, nblocks);
   if (lb >= nblocks) return;
-  mfma_body<G, false>(a, lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
+  mfma_body<G, false, FP8>(a, lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
 }
 
 // One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
 // the rest are private-tail waves (4 per block); both write partials that
 // combine_kernel merges. Matrix-core work and the memory-bound tail overlap.
-template <int G>
+template <int G, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int tiles, int seg_items,
                                                              int n_items, int nsplit) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];
@@ -1275,9 +1396,9 @@ __global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int ti
     const int nblocks = tiles * seg_items * a.Hkv;
     const int lb = xcd_logical(blockIdx.x, nblocks);
     if (lb >= nblocks) return;
-    mfma_body<G, true>(a, lb % tiles, (lb / tiles) % seg_items, lb / (tiles * seg_items), smem);
+    mfma_body<G, true, FP8>(a, lb % tiles, (lb / tiles) % seg_items, lb / (tiles * seg_items), smem);
   } else {
-    tail_bf16_body<G>(a, (blockIdx.x - seg_blocks) * 4 + (threadIdx.x >> 6), n_items, nsplit);
+    tail_bf16_body<G, FP8>(a, (blockIdx.x - seg_blocks) * 4 + (threadIdx.x >> 6), n_items, nsplit);
   }
 }
 
@@ -1370,21 +1491,21 @@ static hipError_t valu_g(int G, int mode, const AttnArgs &a, unsigned items, uns
   return hipErrorInvalidValue;
 }
 
-template <int G>
+template <int G, bool FP8>
 static hipError_t launch_tail(const AttnArgs &a, unsigned items, unsigned splits, hipStream_t stream) {
   if (static_cast<uint64_t>(items) * splits * a.Hkv > 0x7fffffffull) return hipErrorInvalidValue;
   const int whole = a.whole_reqs < static_cast<int>(items) ? a.whole_reqs : static_cast<int>(items);
   const uint64_t waves = tail_items(whole, static_cast<int>(items), static_cast<int>(splits), a.Hkv);
   if (!a.tail_queue) return hipErrorInvalidValue;
   // blocks resident at once on this device (cached per device)
-  static std::atomic<int> resident[64];
+  static std::atomic<int> resident[64];   // one table per kernel instantiation
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   int fit = dev < 64 ? resident[dev].load(std::memory_order_relaxed) : 0;
   if (fit == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tail_bf16_kernel<G>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tail_bf16_kernel<G, FP8>, 256, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -1394,19 +1515,25 @@ static hipError_t launch_tail(const AttnArgs &a, unsigned items, unsigned splits
   const uint64_t blocks = (waves + 3) / 4;
   dim3 grid(static_cast<unsigned>(blocks < static_cast<uint64_t>(fit) ? blocks : fit)), block(256);
   const int n = static_cast<int>(items), ns = static_cast<int>(splits);
-  launch(tail_bf16_kernel<G>, grid, block, 0, stream, a, n, ns);
+  launch(tail_bf16_kernel<G, FP8>, grid, block, 0, stream, a, n, ns);
   return hipGetLastError();
 }
 
-hipError_t decode_tail_bf16(int G, const AttnArgs &a, unsigned batch, unsigned splits, hipStream_t s) {
-  if (batch == 0) return hipSuccess;
+template <bool FP8>
+static hipError_t tail_g(int G, const AttnArgs &a, unsigned batch, unsigned splits, hipStream_t s) {
   switch (G) {
-    case 1: return launch_tail<1>(a, batch, splits, s);
-    case 2: return launch_tail<2>(a, batch, splits, s);
-    case 4: return launch_tail<4>(a, batch, splits, s);
-    case 8: return launch_tail<8>(a, batch, splits, s);
+    case 1: return launch_tail<1, FP8>(a, batch, splits, s);
+    case 2: return launch_tail<2, FP8>(a, batch, splits, s);
+    case 4: return launch_tail<4, FP8>(a, batch, splits, s);
+    case 8: return launch_tail<8, FP8>(a, batch, splits, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t decode_tail_bf16(int G, bool fp8, const AttnArgs &a, unsigned batch, unsigned splits,
+                            hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  return fp8 ? tail_g<true>(G, a, batch, splits, s) : tail_g<false>(G, a, batch, splits, s);
 }
 
 hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, unsigned splits,
@@ -1416,16 +1543,16 @@ hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, u
               : valu_g<float, 64>(G, mode, a, items, splits, s);
 }
 
-template <int G>
+template <int G, bool FP8>
 static hipError_t launch_mfma(const AttnArgs &a, unsigned tiles, unsigned items, hipStream_t s) {
   const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
   if (n > 0x7fffffffull) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(256);
-  launch(attn_mfma_kernel<G>, grid, block, 0, s, a, tiles, items);
+  launch(attn_mfma_kernel<G, FP8>, grid, block, 0, s, a, tiles, items);
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool FP8>
 static hipError_t launch_fused(const AttnArgs &a, unsigned tiles, unsigned seg_items,
                                unsigned n_items, unsigned nsplit, hipStream_t s) {
   const uint64_t seg_blocks = 8 * ((static_cast<uint64_t>(tiles) * seg_items * a.Hkv + 7) / 8);
@@ -1434,33 +1561,45 @@ static hipError_t launch_fused(const AttnArgs &a, unsigned tiles, unsigned seg_i
   const uint64_t tail_blocks =
       (tail_items(whole, static_cast<int>(n_items), static_cast<int>(nsplit), a.Hkv) + 3ull) / 4;
   if (seg_blocks + tail_blocks > 0x7fffffffull) return hipErrorInvalidValue;
-  launch(decode_fused_kernel<G>, dim3(static_cast<unsigned>(seg_blocks + tail_blocks)), dim3(256), 0,
-         s, a, tiles, seg_items, n_items, nsplit);
+  launch(decode_fused_kernel<G, FP8>, dim3(static_cast<unsigned>(seg_blocks + tail_blocks)),
+         dim3(256), 0, s, a, tiles, seg_items, n_items, nsplit);
   return hipGetLastError();
 }
 
-hipError_t decode_fused(int G, const AttnArgs &a, int max_rows, unsigned seg_items,
-                        unsigned n_items, unsigned nsplit, hipStream_t s) {
-  const unsigned tiles = static_cast<unsigned>((max_rows + MF_BM - 1) / MF_BM);
+template <bool FP8>
+static hipError_t fused_g(int G, const AttnArgs &a, unsigned tiles, unsigned seg_items,
+                          unsigned n_items, unsigned nsplit, hipStream_t s) {
   switch (G) {
-    case 1: return launch_fused<1>(a, tiles, seg_items, n_items, nsplit, s);
-    case 2: return launch_fused<2>(a, tiles, seg_items, n_items, nsplit, s);
-    case 4: return launch_fused<4>(a, tiles, seg_items, n_items, nsplit, s);
-    case 8: return launch_fused<8>(a, tiles, seg_items, n_items, nsplit, s);
+    case 1: return launch_fused<1, FP8>(a, tiles, seg_items, n_items, nsplit, s);
+    case 2: return launch_fused<2, FP8>(a, tiles, seg_items, n_items, nsplit, s);
+    case 4: return launch_fused<4, FP8>(a, tiles, seg_items, n_items, nsplit, s);
+    case 8: return launch_fused<8, FP8>(a, tiles, seg_items, n_items, nsplit, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t mfma(int G, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
-  if (items == 0 || max_rows <= 0) return hipSuccess;
+hipError_t decode_fused(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned seg_items,
+                        unsigned n_items, unsigned nsplit, hipStream_t s) {
   const unsigned tiles = static_cast<unsigned>((max_rows + MF_BM - 1) / MF_BM);
+  return fp8 ? fused_g<true>(G, a, tiles, seg_items, n_items, nsplit, s)
+             : fused_g<false>(G, a, tiles, seg_items, n_items, nsplit, s);
+}
+
+template <bool FP8>
+static hipError_t mfma_g(int G, const AttnArgs &a, unsigned tiles, unsigned items, hipStream_t s) {
   switch (G) {
-    case 1: return launch_mfma<1>(a, tiles, items, s);
-    case 2: return launch_mfma<2>(a, tiles, items, s);
-    case 4: return launch_mfma<4>(a, tiles, items, s);
-    case 8: return launch_mfma<8>(a, tiles, items, s);
+    case 1: return launch_mfma<1, FP8>(a, tiles, items, s);
+    case 2: return launch_mfma<2, FP8>(a, tiles, items, s);
+    case 4: return launch_mfma<4, FP8>(a, tiles, items, s);
+    case 8: return launch_mfma<8, FP8>(a, tiles, items, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
+  if (items == 0 || max_rows <= 0) return hipSuccess;
+  const unsigned tiles = static_cast<unsigned>((max_rows + MF_BM - 1) / MF_BM);
+  return fp8 ? mfma_g<true>(G, a, tiles, items, s) : mfma_g<false>(G, a, tiles, items, s);
 }
 
 hipError_t combine(bool bf16, const AttnArgs &a, int batch, int Dv, hipStream_t s) {

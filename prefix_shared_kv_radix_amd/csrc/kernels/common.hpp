@@ -43,6 +43,31 @@ __device__ __forceinline__ float fp8_to_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), SEL);
 }
 
+// Two E4M3FN bytes of w (bytes 0,1 or, with HI, 2,3) -> a packed bf16 pair, exactly:
+// every E4M3 value (4 significant bits, exponents -9..8) is a bf16 value, and a scale
+// operand of 1 leaves it unchanged.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI));
+}
+
+// Sixteen E4M3FN bytes times `scale`, rounded to bf16 (nearest even): two 16-byte rows
+// of packed bf16 pairs, lo = values 0..7, hi = values 8..15.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4 &w, float scale, u32x4 &lo, u32x4 &hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+    out[2 * i] = cvt_bf16x2(a[0] * scale, a[1] * scale);
+    out[2 * i + 1] = cvt_bf16x2(b[0] * scale, b[1] * scale);
+  }
+  lo = u32x4{out[0], out[1], out[2], out[3]};
+  hi = u32x4{out[4], out[5], out[6], out[7]};
+}
+
 // Sum over each group of 16 consecutive lanes; every lane of the group gets the sum.
 // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
 __device__ __forceinline__ float sum16(float x) {
@@ -69,6 +94,16 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
 __device__ __forceinline__ int32_t ld_async4(const int32_t *p) {
   int32_t v;
   asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ float ld_async4f(const float *p) {
+  float v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x2 ld_async8(const void *p) {
+  u32x2 v;
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
 template <int OFF>

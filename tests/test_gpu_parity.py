@@ -328,6 +328,49 @@ def test_extend_batch_with_fully_cached_prompts(dtype):
     assert chk.checked > 0
 
 
+@pytest.mark.parametrize("use_plan,splits", [(True, 0), (False, 1), (False, 3), (True, 2)])
+def test_few_shot_fp8_kv_small(use_plan, splits):
+    """GQA-128 with fp8 E4M3 K/V (one scale per token): extend tiles and shared-segment
+    tiles stage the bytes and convert them (times the scale) to bf16; the private tails
+    convert them exactly and apply the scale to score and probability. All outputs."""
+    w = few_shot(32, gqa128_shape("fp8"), 300, 24, 37, 9, q_rows=4096)
+    _run(w, Checker(w), use_plan=use_plan, num_splits=splits)
+
+
+def test_agent_fp8_kv_segment_chunks():
+    """fp8 K/V through two nested shared segments cut into key chunks."""
+    w = agent_branch(33, gqa128_shape("fp8"), 3, 200, 4, 70, 3, 6, q_rows=4096)
+    _run(w, Checker(w, extend_sample=6), split_keys=100)
+
+
+@pytest.mark.parametrize("hq,use_plan", [(8, True), (16, False), (64, True), (64, False)])
+def test_fp8_kv_head_groups(hq, use_plan):
+    """fp8 K/V with 1, 2 and 8 query heads per KV head (8 heads: compiler-placed waits)."""
+    import dataclasses
+    shape = dataclasses.replace(gqa128_shape("fp8"), num_q_heads=hq)
+    w = few_shot(34, shape, 130, 6, 21, 3, q_rows=512)
+    _run(w, Checker(w), use_plan=use_plan)
+
+
+def test_fp8_kv_tail_work_queue():
+    """fp8 private tails drawn from the work queue (more items than resident waves)."""
+    w = few_shot(35, gqa128_shape("fp8"), 600, 96, 40, 3, q_rows=4096)
+    _run(w, Checker(w), use_plan=False, num_splits=8)
+
+
+def test_fp8_kv_extend_with_fully_cached_prompts():
+    w = mixed_hits(36, gqa128_shape("fp8"), 150, 40, 3)
+    _run(w, Checker(w))
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_fp8_kv_full_size(n):
+    """Configs 2 and 4 with fp8 K/V: every request at the first and last decode step."""
+    w = config(n, "fp8")
+    last = {2: 127, 4: 255}[n]
+    _run(w, Checker(w, extend_sample=3, decode_steps={0, last}))
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_mla_small(kv):
     """MLA decode (128 heads, one 576-dim latent KV head, V = first 512 dims): three

@@ -193,3 +193,25 @@ def test_request_kv_mla_values_are_key_prefix():
     w = mla_groups(9, "fp8", 2, 8, 2, 4, 2, q_rows=64)
     k, v = request_kv(w, w.full_kv_ids(w.phases[1].rids[0]))
     np.testing.assert_array_equal(v, k[:, :, :512])
+
+
+def test_request_kv_gqa_fp8_shares_the_token_scale():
+    """GQA fp8: a token's K and V rows (all KV heads) are quantised with one scale,
+    amax over both / 448, and the oracle decodes both with it: the decoded values sit
+    within E4M3's rounding of the unquantised N(0,1) table values, and the largest
+    magnitude over a token's K and V is reproduced exactly."""
+    from workloads import _normal, few_shot, gqa128_shape
+    w = few_shot(2, gqa128_shape("fp8"), 20, 2, 4, 1, q_rows=64)
+    s = w.shape
+    k_raw = _normal(np.random.default_rng([w.seed, 1]), (w.table_rows, s.num_kv_heads, s.head_dim_qk))
+    v_raw = _normal(np.random.default_rng([w.seed, 2]), (w.table_rows, s.num_kv_heads, s.head_dim_v))
+    ids = w.full_kv_ids(w.phases[1].rids[0])
+    k, v = request_kv(w, ids)
+    rows = w.kv_rows(ids)
+    kr, vr = k_raw[rows].astype(np.float64), v_raw[rows].astype(np.float64)
+    amax = np.maximum(np.abs(kr).reshape(len(rows), -1).max(1), np.abs(vr).reshape(len(rows), -1).max(1))
+    sc = (amax / 448.0)[:, None, None]
+    assert np.all(np.abs(k - kr) <= np.abs(kr) / 16 + sc * 2.0 ** -9 + 1e-12)
+    assert np.all(np.abs(v - vr) <= np.abs(vr) / 16 + sc * 2.0 ** -9 + 1e-12)
+    both = np.maximum(np.abs(k).reshape(len(rows), -1).max(1), np.abs(v).reshape(len(rows), -1).max(1))
+    np.testing.assert_allclose(both, amax, rtol=1e-6)

@@ -154,9 +154,13 @@ class Workload:
                 k = f32_to_bf16_bits(k)
                 v = None if v is None else f32_to_bf16_bits(v)
             elif s.kv_dtype == "fp8":
-                if v is not None:
-                    raise ValueError("fp8 tables are only defined for the MLA layout")
-                k, scale = quantize_e4m3_rows(k)
+                if v is None:
+                    k, scale = quantize_e4m3_rows(k)
+                else:
+                    # one scale per token: the token's K and V rows (all KV heads) together
+                    kv, scale = quantize_e4m3_rows(np.concatenate([k, v], axis=-1))
+                    k = np.ascontiguousarray(kv[..., :s.head_dim_qk])
+                    v = np.ascontiguousarray(kv[..., s.head_dim_qk:])
             else:
                 raise ValueError(s.kv_dtype)
             self._cache["kv"] = (k, v, scale)
@@ -237,9 +241,10 @@ def tiny_shape() -> AttnShape:
     return AttnShape(4, 4, 64, 64, "f32", "f32", False, 1.0 / 8.0)
 
 
-def gqa128_shape() -> AttnShape:
-    """Llama-3-8B attention shape: 32 query heads, 8 KV heads, head dim 128, bf16."""
-    return AttnShape(32, 8, 128, 128, "bf16", "bf16", False, 1.0 / math.sqrt(128.0))
+def gqa128_shape(kv_dtype: str = "bf16") -> AttnShape:
+    """Llama-3-8B attention shape: 32 query heads, 8 KV heads, head dim 128, bf16 queries;
+    K/V bf16, or fp8 E4M3 with one scale per token."""
+    return AttnShape(32, 8, 128, 128, "bf16", kv_dtype, False, 1.0 / math.sqrt(128.0))
 
 
 def mla_shape(kv_dtype: str = "bf16") -> AttnShape:
@@ -501,16 +506,18 @@ CONFIG_NAMES = {
 def config(n: int, variant: str = "") -> Workload:
     """Full-size workload for configuration ``n`` (seed = n).
 
-    variant: for 3, 'A' (chat tree extend under churn) or 'B' (scattered decode);
-    for 4, '' (branching), 'cyclic', 'grouped' or 'cyclic_lpf';
+    variant: for 2, '' (bf16 K/V) or 'fp8' (E4M3 K/V, one scale per token);
+    for 3, 'A' (chat tree extend under churn) or 'B' (scattered decode);
+    for 4, '' (branching), 'fp8' (branching, E4M3 K/V), 'cyclic', 'grouped' or 'cyclic_lpf';
     for 5, 'bf16' or 'fp8'.
     """
     if n == 1:
         return few_shot(1, tiny_shape(), 64, 8, 32, 16, pool_slots=1024, name="tiny_fp32",
                         q_rows=1024)
     if n == 2:
-        return few_shot(2, gqa128_shape(), 2048, 256, 128, 128, pool_slots=67584,
-                        name="few_shot_gqa128")
+        kv = variant or "bf16"
+        return few_shot(2, gqa128_shape(kv), 2048, 256, 128, 128, pool_slots=67584,
+                        name="few_shot_gqa128" + ("" if kv == "bf16" else "_fp8"))
     if n == 3:
         if variant in ("", "A"):
             return chat_tree(3, gqa128_shape(), 64, 8, 64, 256, 0.7, name="chat_tree_3A")
@@ -519,9 +526,10 @@ def config(n: int, variant: str = "") -> Workload:
                                table_rows=1 << 18, name="chat_decode_3B")
         raise ValueError(variant)
     if n == 4:
-        if variant == "":
-            return agent_branch(4, gqa128_shape(), 16, 4096, 8, 512, 4, 256,
-                                name="agent_branch_4")
+        if variant in ("", "fp8"):
+            kv = variant or "bf16"
+            return agent_branch(4, gqa128_shape(kv), 16, 4096, 8, 512, 4, 256,
+                                name="agent_branch_4" + ("" if kv == "bf16" else "_fp8"))
         order, policy = {"cyclic": ("cyclic", "fcfs"), "grouped": ("grouped", "fcfs"),
                          "cyclic_lpf": ("cyclic", "lpf")}[variant]
         return cyclic_stream(4, gqa128_shape(), 5, 2048, 2, 4, order, policy,
