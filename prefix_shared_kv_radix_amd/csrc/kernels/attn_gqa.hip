@@ -516,9 +516,7 @@ __device__ __forceinline__ void merge_requests_bf16(const AttnArgs &a, const int
 #ifndef RADIX_TAIL_STAGES
 #define RADIX_TAIL_STAGES 3
 #endif
-#ifndef RADIX_TAIL_GROUP
-#define RADIX_TAIL_GROUP 1
-#endif
+
 
 __device__ __forceinline__ int32_t take_ticket(int32_t *q);
 
@@ -553,19 +551,9 @@ __device__ __forceinline__ void tail_bf16_body(const AttnArgs &a, int w, int n_i
   const bool one = w < whole * a.Hkv;
   const int wr = one ? w : w - whole * a.Hkv;
   const int ns_tail = one ? 1 : nsplit;   // private parts of this request
-  int kvh = wr % a.Hkv;
+  const int kvh = wr % a.Hkv;
   const int split = (wr / a.Hkv) % ns_tail;
-  int b = (one ? 0 : whole) + wr / (a.Hkv * ns_tail);
-  // Requests read whole are taken RADIX_TAIL_GROUP at a time per KV head: the waves of one
-  // block then read the same KV head of consecutive requests, which share their
-  // key prefix when consecutive requests branch off one tree node (the rows come once
-  // from HBM, then from the shared caches).
-  constexpr int TG = RADIX_TAIL_GROUP;
-  if (TG > 1 && one && w < (whole / TG) * TG * a.Hkv) {
-    const int r = w % (TG * a.Hkv);
-    kvh = r / TG;
-    b = (w / (TG * a.Hkv)) * TG + r % TG;
-  }
+  const int b = (one ? 0 : whole) + wr / (a.Hkv * ns_tail);
 
   const int hi = a.seq_lens[b];
   const int lo = a.private_start ? a.private_start[b] : 0;

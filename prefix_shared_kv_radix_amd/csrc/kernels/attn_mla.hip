@@ -5,7 +5,8 @@
 // Requests sharing a radix-tree prefix run at the same time on the same XCD, so the
 // shared rows come from that XCD's L2 after the first read.
 // KV rows are bf16, or OCP E4M3 bytes with one fp32 scale per token (KV cache FP8,
-// same section), dequantised to bf16 as they are staged into LDS.
+// same section): the bytes are staged raw and converted exactly to bf16, and each
+// key's scale multiplies its score and its probability.
 //
 // Block = one request's 128 heads over one key range, 8 waves. Waves w and w+4 share
 // the 32 heads 32*(w%4) .. +31 and split the work by dimension: wave half 0 takes QK
@@ -14,8 +15,9 @@
 // the pair swaps partials through LDS and both add them in the same order, so both
 // run the identical online softmax; then O^T += V^T P^T over the wave's value dims.
 // Per wave that is 72 registers of Q and 128 accumulator registers of O, which fits
-// two waves per SIMD. Tiles are double-buffered in LDS (bf16 rows go straight from
-// global memory to LDS; fp8 rows pass through registers to be dequantised). With one
+// two waves per SIMD. bf16 tiles are double-buffered in LDS (rows go straight from
+// global memory to LDS); fp8 rows go straight to a staging tile while the one bf16 tile
+// is in use, and are converted into it between tiles. With one
 // chunk per request the block writes the output; with several, partials (o, lse)
 // that combine_kernel merges.
 #include "attn_args.hpp"
@@ -84,22 +86,32 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
 
   // ---- tile loads. bf16: region-A row J by wave J % 8 (lane i brings logical chunk
   // i ^ fA(J)); region B by waves 0..3 (lane i: row 8*wave + i/8, chunk i%8 ^ fB(row)).
-  // Lane r holds the slot of row r (lanes 32..63 repeat). fp8: 16 threads per row,
-  // thread converts 8-byte groups fsub + 16i (< 72) of row tid/16 into bf16 chunks.
+  // Lane r holds the slot of row r (lanes 32..63 repeat).
+  // fp8: the raw 576-byte rows go straight to a linear staging tile (18 direct loads of
+  // 64 16-byte chunks, spread over the waves), the tile's 32 key scales to a scale
+  // array; once landed, the rows are converted exactly to bf16 (every E4M3 value is a
+  // bf16 value) into the one bf16 tile the matrix code reads, and each key's scale is
+  // applied to its score and its probability instead.
   const uint8_t *kv = static_cast<const uint8_t *>(a.kv);
   const int last = hi - 1;
-  const int frow = tid >> 4, fsub = tid & 15;
   int32_t sl;
-  u32x2 raw[FP8 ? 5 : 1];
-  float rscale = 0.f;
-  auto load_slots = [&](int kt) { sl = rtt_row[min(kt + (FP8 ? frow : (lane & 31)), last)]; };
+  uint8_t *stg = smem[2];                                        // fp8 staging, 18 KB
+  float *scl = reinterpret_cast<float *>(smem[2] + kBN * kDqk);   // fp8 scales [4][64]
+  auto load_slots = [&](int kt) { sl = rtt_row[min(kt + (lane & 31), last)]; };
   auto issue = [&](int kt, int stage) {
     if (FP8) {
-      const uint8_t *src = kv + static_cast<int64_t>(sl) * kDqk;
-#pragma unroll
-      for (int i = 0; i < 5; ++i)
-        raw[i] = *reinterpret_cast<const u32x2 *>(src + 8 * min(fsub + 16 * i, 71));
-      rscale = (kt + frow < hi) ? a.kv_scale[sl] : 0.f;
+      for (int i = wave; i < kBN * kDqk / 1024; i += 8) {   // 18 loads of 1 KB
+        const int ch = 64 * i + lane;                        // row ch / 36, chunk ch % 36
+        const int r = ch / 36, c = ch - 36 * r;
+        const int64_t slot = __builtin_amdgcn_ds_bpermute(r << 2, sl);
+        lds_load16(kv + slot * kDqk + c * 16, stg + 1024 * i);
+      }
+      if (wave == 0)
+        __builtin_amdgcn_global_load_lds(
+            a.kv_scale + sl,
+            reinterpret_cast<__attribute__((address_space(3))) void *>(
+                reinterpret_cast<uintptr_t>(scl + 64 * stage)),
+            4, 0, 0);
     } else {
 #pragma unroll
       for (int jj = 0; jj < kBN / 8; ++jj) {
@@ -115,35 +127,42 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
       }
     }
   };
-  auto stash = [&](int stage) {   // fp8 only: dequantise the registers into the bf16 tile
-    if (FP8) {
-      int tv = tid;
-      asm volatile("" : "+v"(tv));
-      const int frow = tv >> 4, fsub = tv & 15;
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const int c = fsub + 16 * i;
-        if (c < 72) {
-          const uint32_t x = raw[i][0], y = raw[i][1];
-          const u32x4 w = u32x4{cvt_bf16x2(fp8_to_f32<0>(x) * rscale, fp8_to_f32<1>(x) * rscale),
-                                cvt_bf16x2(fp8_to_f32<2>(x) * rscale, fp8_to_f32<3>(x) * rscale),
-                                cvt_bf16x2(fp8_to_f32<0>(y) * rscale, fp8_to_f32<1>(y) * rscale),
-                                cvt_bf16x2(fp8_to_f32<2>(y) * rscale, fp8_to_f32<3>(y) * rscale)};
-          *reinterpret_cast<u32x4 *>(&smem[stage][c < 64 ? offA(frow, c) : offB(frow, c - 64)]) = w;
-        }
-      }
+  // fp8: staged rows -> bf16 tile `dst` (the caller has waited for the loads). Each wave
+  // converts exactly the chunks its own loads brought in, so it needs no barrier before
+  // reusing the staging tile for the next loads, only its own LDS reads done.
+  auto convert = [&](int dst) {
+    for (int ch = tid; ch < kBN * 36; ch += 512) {   // wave-uniform trip count
+      const int r = ch / 36, c = ch - 36 * r;
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(stg + 16 * ch);
+      const u32x4 lo16 = u32x4{fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                               fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
+      const u32x4 hi16 = u32x4{fp8x2_to_bf16x2<false>(w[2]), fp8x2_to_bf16x2<true>(w[2]),
+                               fp8x2_to_bf16x2<false>(w[3]), fp8x2_to_bf16x2<true>(w[3])};
+      const int o0 = c < 32 ? offA(r, 2 * c) : offB(r, 2 * (c - 32));
+      const int o1 = c < 32 ? offA(r, 2 * c + 1) : offB(r, 2 * (c - 32) + 1);
+      *reinterpret_cast<u32x4 *>(&smem[dst][o0]) = lo16;
+      *reinterpret_cast<u32x4 *>(&smem[dst][o1]) = hi16;
     }
   };
 
+  // bf16: tile t+1's loads are in flight while tile t is used (two LDS buffers).
+  // fp8: tile t+2's raw bytes are in flight while tile t is used, and tile t+1, landed,
+  // is converted into the other bf16 buffer at the start of iteration t, overlapping the
+  // other waves' matrix work (key scales: four buffers, tile t in t % 4).
   const int ntiles = hi > lo ? (hi - lo + kBN - 1) / kBN : 0;
   if (ntiles > 0) {
     load_slots(lo);
     issue(lo, 0);
+    if (ntiles > 1) load_slots(lo + kBN);
     if (FP8) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      stash(0);
+      convert(0);
+      if (ntiles > 1) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own staging reads done
+        issue(lo + kBN, 1);
+        if (ntiles > 2) load_slots(lo + 2 * kBN);
+      }
     }
-    if (ntiles > 1) load_slots(lo + kBN);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -152,7 +171,14 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int kt = lo + t * kBN;
-    if (t + 1 < ntiles) {
+    if (FP8) {
+      if (t + 1 < ntiles) convert(buf ^ 1);   // tile t+1 (landed at the last barrier)
+      if (t + 2 < ntiles) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(kt + 2 * kBN, (t + 2) & 3);
+        if (t + 3 < ntiles) load_slots(kt + 3 * kBN);
+      }
+    } else if (t + 1 < ntiles) {
       issue(kt + kBN, buf ^ 1);
       if (t + 2 < ntiles) load_slots(kt + 2 * kBN);
     }
@@ -201,6 +227,16 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
         sc[i] = key < hi ? sc[i] : -INFINITY;
       }
     }
+    // fp8: each key's scale (> 0) on its score; keys of sc[i]: 8*(i>>2) + 4h + (i&3)
+    const float *ks = scl + 64 * (t & 3) + 4 * h;
+    if (FP8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(ks + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[4 * q + e] *= s4[e];
+      }
+    }
     // raw scores: the scale (> 0) is applied to the maximum and inside the exponent
     float mx = -INFINITY;
 #pragma unroll
@@ -223,6 +259,14 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
       rs += p;
     }
     l_run += rs;   // this half's keys; the two halves are added after the loop
+    if (FP8) {   // the value rows' scales go with their probabilities
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(ks + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[4 * q + e] *= s4[e];
+      }
+    }
     bf16x8 pb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -262,10 +306,6 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[j], o[d],
                                                         0, 0, 0);
       }
-    }
-    if (FP8 && t + 1 < ntiles) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      stash(buf ^ 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -307,7 +347,8 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
 template <bool FP8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][kTileB];
+  // bf16 tiles double-buffered; fp8 adds a staging tile and its key scales
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FP8 ? 3 : 2][kTileB];
   __shared__ __attribute__((aligned(16))) f32x4 xs[8][4][64];   // partial scores per wave
 
   // ---- work item: requests in plan order (members of one shared segment are
