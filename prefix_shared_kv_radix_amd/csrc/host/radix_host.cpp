@@ -694,8 +694,17 @@ radix_status radix_tree_decode_plan(const radix_tree *tree, const radix_node *no
     maxsh = std::max(maxsh, rank);
     maxparts = std::max(maxparts, parts);
   }
-  // requests grouped by their root-most shared segment (segment creation order), then
-  // the requests without any, in batch order
+  // Launch order: segments whose key chunks are longest first (longest work first), so
+  // their blocks start at once instead of behind many short ones; ties keep creation
+  // order. Every array below follows this order.
+  auto chunk_len = [](const Seg &g) {
+    const int32_t len = g.end - g.start;
+    return ((len + g.chunks - 1) / g.chunks + 63) / 64 * 64;
+  };
+  std::stable_sort(segs.begin(), segs.end(),
+                   [&](const Seg &x, const Seg &y) { return chunk_len(x) > chunk_len(y); });
+  // requests grouped by their root-most shared segment (in the order above), then the
+  // requests without any, in batch order
   {
     int32_t k = 0;
     std::vector<uint8_t> placed(static_cast<size_t>(batch), 0);

@@ -518,6 +518,7 @@ __device__ __forceinline__ void merge_requests_bf16(const AttnArgs &a, const int
 #endif
 
 
+
 __device__ __forceinline__ int32_t take_ticket(int32_t *q);
 
 // One private-tail item w = (request, split, KV head) on one wave. With a work queue
@@ -1362,6 +1363,12 @@ __device__ __forceinline__ int xcd_logical(int bid, int nblocks) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// Blocks of the shared-segment part of a fused decode launch: every XCD gets room for
+// ceil(groups / 8) groups of `tiles` blocks.
+__host__ __device__ __forceinline__ int seg_block_count(int tiles, int groups) {
+  return 8 * tiles * ((groups + 7) / 8);
+}
+
 // extend: logical block -> (tile, request, kvh), tile fastest
 template <int G, bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
@@ -1379,12 +1386,17 @@ template <int G, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int tiles, int seg_items,
                                                              int n_items, int nsplit) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];
-  const int seg_blocks = 8 * ((tiles * seg_items * a.Hkv + 7) / 8);
+  const int groups = seg_items * a.Hkv;   // (chunk, KV head) pairs, `tiles` blocks each
+  const int seg_blocks = seg_block_count(tiles, groups);
   if (static_cast<int>(blockIdx.x) < seg_blocks) {
-    const int nblocks = tiles * seg_items * a.Hkv;
-    const int lb = xcd_logical(blockIdx.x, nblocks);
-    if (lb >= nblocks) return;
-    mfma_body<G, true, FP8>(a, lb % tiles, (lb / tiles) % seg_items, lb / (tiles * seg_items), smem);
+    // Block b runs on XCD b % 8 as the (b / 8)-th there. Group g = (chunk, KV head), KV
+    // head fastest, chunks in plan order (longest keys first), goes to XCD g % 8 whole:
+    // its tiles read the same K/V rows, through one L2. The longest groups are dispatched
+    // first on every XCD.
+    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const int g = xcd + 8 * (k / tiles);
+    if (g >= groups) return;
+    mfma_body<G, true, FP8>(a, k % tiles, g / a.Hkv, g % a.Hkv, smem);
   } else {
     tail_bf16_body<G, FP8>(a, (blockIdx.x - seg_blocks) * 4 + (threadIdx.x >> 6), n_items, nsplit);
   }
@@ -1543,7 +1555,9 @@ static hipError_t launch_mfma(const AttnArgs &a, unsigned tiles, unsigned items,
 template <int G, bool FP8>
 static hipError_t launch_fused(const AttnArgs &a, unsigned tiles, unsigned seg_items,
                                unsigned n_items, unsigned nsplit, hipStream_t s) {
-  const uint64_t seg_blocks = 8 * ((static_cast<uint64_t>(tiles) * seg_items * a.Hkv + 7) / 8);
+  const uint64_t groups = static_cast<uint64_t>(seg_items) * a.Hkv;
+  const uint64_t seg_blocks = 8ull * tiles * ((groups + 7) / 8);   // = seg_block_count()
+  if (seg_blocks > 0x7fffffffull) return hipErrorInvalidValue;
   if (static_cast<uint64_t>(n_items) * nsplit * a.Hkv > 0x7fffffffull) return hipErrorInvalidValue;
   const int whole = a.whole_reqs < static_cast<int>(n_items) ? a.whole_reqs : static_cast<int>(n_items);
   const uint64_t tail_blocks =
