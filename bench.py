@@ -48,6 +48,8 @@ def parse():
                         "1, 2, 2fp8, 3A, 3B, 4fp8, 5bf16, 5fp8")
     p.add_argument("--no-plan", action="store_true", help="decode without shared segments")
     p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--split-keys", type=int, default=None,
+                   help="key chunk length of long shared segments (default: chosen per round)")
     p.add_argument("--min-members", type=int, default=2,
                    help="members a shared segment needs to be read once for all of them")
     p.add_argument("--layers", type=int, default=4,
@@ -80,13 +82,14 @@ class Episode:
     """Pre-staged device inputs for every round of a workload, and one timed pass."""
 
     def __init__(self, w, use_plan, splits, layers=1, schedule="overlap", ahead=1,
-                 min_members=2):
+                 min_members=2, split_keys=None):
         import torch
         from prefix_shared_kv_radix_amd import _lib
         from prefix_shared_kv_radix_amd.runner import DeviceState, Engine, build_decode_plan
         self.torch, self._lib, self.build_plan = torch, _lib, build_decode_plan
         self.w, self.use_plan, self.splits = w, use_plan, splits
         self.min_members = min_members
+        self.split_keys = split_keys
         # "overlap": the host prepares decode step s+1 (slot allocation, pinned slot rows,
         # launches) while step s runs, and waits only for step s-1 (whose outputs a server
         # would read); "sync": the host waits for every step before preparing the next
@@ -94,7 +97,7 @@ class Episode:
         self.ahead = max(1, int(ahead))
         self.step_evt = [_lib.Fence() for _ in range(self.ahead + 1)]
         # host-only pass: the rounds (and their plans) are deterministic
-        dry = Engine(w, min_members=min_members).run()
+        dry = Engine(w, min_members=min_members, split_keys=split_keys).run()
         self.rounds = dry.rounds
         dev = "cuda"
         max_batch = max(len(r.admissions) for r in dry.rounds)
@@ -184,8 +187,8 @@ class Episode:
                 raise RuntimeError("episode diverged from its dry run")
             plan_dev, keep = (None, [])
             if ph.n_decode and self.use_plan and B > 1:
-                plan_dev, keep = _lib.device_plan(self.build_plan(tree, nodes, self.min_members),
-                                                  d.device)
+                plan_dev, keep = _lib.device_plan(
+                    self.build_plan(tree, nodes, self.min_members, self.split_keys), d.device)
             if ph.extend != "host":
                 rtt_pin[:B].copy_(torch.from_numpy(rows))
                 d.rtt[:B].copy_(rtt_pin[:B], non_blocking=True)
@@ -426,6 +429,25 @@ def cpu_baseline(w, seconds):
             "host_cores_visible": len(os.sched_getaffinity(0))}
 
 
+def read_bandwidth(mib=1024, reps=10):
+    """Device read rate of a plain reduction over `mib` MiB of fp32 (bytes read per second,
+    median of `reps` event-timed sums): the read-only ceiling for gather-heavy kernels."""
+    import torch
+    n = (mib << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    x.sum()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        x.sum()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    del x
+    return 4.0 * n / float(np.median(times)) / 1e9
+
+
 def copy_bandwidth(mib=1024, reps=10):
     """Device-to-device copy rate (read + write bytes per second) of a plain copy of
     `mib` MiB, median of `reps` event-timed copies: the practical HBM ceiling next to
@@ -472,7 +494,7 @@ def main():
         print("--layers must be at least 1", file=sys.stderr)
         sys.exit(2)
     ep = Episode(w, not args.no_plan, args.splits, args.layers, args.schedule, args.ahead,
-                 args.min_members)
+                 args.min_members, args.split_keys)
     torch.cuda.synchronize()
     print(f"[bench] staged {w.name}: {len(ep.rounds)} rounds", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -539,9 +561,12 @@ def main():
         roof = {"bound": "hbm", "achieved": byt / t_dom / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     copy_gbps = copy_bandwidth()
+    read_gbps = read_bandwidth()
     if roof["bound"] == "hbm":
         roof["copy_gbps"] = copy_gbps
         roof["frac_of_copy"] = roof["achieved"] / copy_gbps
+        roof["read_gbps"] = read_gbps
+        roof["frac_of_read"] = roof["achieved"] / read_gbps
     roof["kernel"] = dom
     roof["avg_launch_us"] = 1e3 * kern[dom][1] / kern[dom][0]
     roof["algorithmic_bytes_per_launch"] = byt / (kern[dom][0] / (args.steps * L))
@@ -578,6 +603,7 @@ def main():
         "decode_algorithmic_gbps": dec_bytes / (dec_ms / 1e3) / 1e9 if dec_ms else None,
         "decode_hbm_frac_of_peak": dec_bytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBPS if dec_ms else None,
         "copy_gbps": copy_gbps,
+        "read_gbps": read_gbps,
         "extend_mfma_frac_of_peak": ext_flops / (ext_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS if ext_ms else None,
         "kernels": kernels,
         "roofline": roof,

@@ -6,12 +6,15 @@ compares the outputs with the oracle's exact attention over each request's
 own keys (fp64): max-abs <= 1e-4 for fp32, <= 2e-2 for bf16 I/O with fp32
 accumulation; LSE within 1e-5 / 1e-3.
 
-fp8 K/V (E4M3 bytes times a per-token scale): the kernel rounds each dequantised
-element to a bf16 MMA operand (round to nearest even, relative error at most
-2^-8), so a score moves by at most sm_scale * sum_i |q_i k_i| * 2^-8 and the LSE,
-a smooth maximum of the scores, by at most the largest such move over the keys it
-sees. The LSE tolerance of an fp8 row is that bound, computed from the row's own
-query and dequantised keys, on top of the bf16 tolerance.
+fp8 K/V (E4M3 bytes times a per-token scale): the GQA extend and shared-segment
+tiles round each dequantised element to a bf16 MMA operand (round to nearest even,
+relative error at most 2^-8), so a score moves by at most
+sm_scale * sum_i |q_i k_i| * 2^-8 and the LSE, a smooth maximum of the scores, by
+at most the largest such move over the keys it sees. The LSE tolerance of a GQA
+fp8 row is that bound, computed from the row's own query and dequantised keys, on
+top of the bf16 tolerance. The MLA kernel converts E4M3 to bf16 exactly and applies
+each key's scale to its score and probability, so its fp8 rows get the bf16
+tolerance alone.
 
 Decode checks are gathered while the episode runs and computed afterwards, one
 oracle call per request for all its checked positions, on a thread pool.
@@ -59,7 +62,9 @@ class Checker:
         self.decode_steps = decode_steps
         self.decode_sample = decode_sample
         self.tol_o, self.tol_l = TOL[w.shape.q_dtype]
-        self.fp8 = w.shape.kv_dtype == "fp8"
+        # MLA converts E4M3 exactly and scales scores and probabilities: the bf16 LSE
+        # tolerance alone; GQA fp8 tiles round (value x scale) to bf16: add the bound
+        self.fp8 = w.shape.kv_dtype == "fp8" and not w.shape.v_is_k_prefix
         self.worst = 0.0
         self.checked = 0
         self.pending = {}   # rid -> [(position, o, lse)]
