@@ -227,45 +227,6 @@ __device__ __forceinline__ void lds_tr16_x16(u32x2 (&r)[16], const uint32_t (&a)
       : "memory");
 }
 
-// Sixteen transposed LDS reads issued without waiting; lds_wait16 (tied to the same
-// registers, so nothing reads them earlier) completes them. LDS reads of one wave
-// return in order, so any wait the compiler places for its own later LDS operations
-// also covers these.
-__device__ __forceinline__ void lds_tr16_issue16(u32x2 (&r)[16], const uint32_t (&a)[16]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %17\n\t"
-      "ds_read_b64_tr_b16 %2, %18\n\t"
-      "ds_read_b64_tr_b16 %3, %19\n\t"
-      "ds_read_b64_tr_b16 %4, %20\n\t"
-      "ds_read_b64_tr_b16 %5, %21\n\t"
-      "ds_read_b64_tr_b16 %6, %22\n\t"
-      "ds_read_b64_tr_b16 %7, %23\n\t"
-      "ds_read_b64_tr_b16 %8, %24\n\t"
-      "ds_read_b64_tr_b16 %9, %25\n\t"
-      "ds_read_b64_tr_b16 %10, %26\n\t"
-      "ds_read_b64_tr_b16 %11, %27\n\t"
-      "ds_read_b64_tr_b16 %12, %28\n\t"
-      "ds_read_b64_tr_b16 %13, %29\n\t"
-      "ds_read_b64_tr_b16 %14, %30\n\t"
-      "ds_read_b64_tr_b16 %15, %31"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
-        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]),
-        "v"(a[15])
-      : "memory");
-}
-__device__ __forceinline__ void lds_wait16(u32x2 (&r)[16]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
-                 "+v"(r[6]), "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]),
-                 "+v"(r[12]), "+v"(r[13]), "+v"(r[14]), "+v"(r[15])
-               :
-               : "memory");
-}
-
 // Four transposed LDS reads and the wait for them (as lds_tr16_x8, fewer registers).
 __device__ __forceinline__ void lds_tr16_x4(u32x2 (&r)[4], const uint32_t (&a)[4]) {
   asm volatile(
