@@ -991,6 +991,38 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
                                    16, 0, 0);
 }
 
+// The sixteen V^T operand reads of two 32-dim value blocks for all 64 keys of a tile, and
+// the wait for them: r[8*dd + 2*q + p] = transposed read at b[2*dd + p] + 4096*q (keys
+// 16q .. 16q+15 lie 16 rows = 4096 bytes apart), the key offsets as immediate offsets of
+// the reads instead of one address add per read. Assembly for the reason given at
+// lds_tr16_x4.
+__device__ __forceinline__ void lds_tr16_v64(u32x2 (&r)[16], uint32_t b0, uint32_t b1, uint32_t b2,
+                                             uint32_t b3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %6, %16 offset:12288\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:12288\n\t"
+      "ds_read_b64_tr_b16 %8, %18\n\t"
+      "ds_read_b64_tr_b16 %9, %19\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %18 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %13, %19 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %14, %18 offset:12288\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:12288\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+      : "memory");
+}
+
 // 128 query rows (4 waves x 32) against 64-key tiles, bf16 MFMA 32x32x16.
 //   S^T = K Q^T : A = K rows from LDS, B = Q in registers; a lane holds one query row
 //                 (column) and 16 keys, so the row softmax is lane-local plus one
@@ -1095,18 +1127,24 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       sl[j] = rtt_row[min(kt + r, last)];
     }
   };
+  // byte offset of a slot's row plus this lane's chunk: one unsigned 32 x 32 -> 64-bit
+  // multiply-add (slots are non-negative), shared by the K and V loads
+  auto row_off = [&](int32_t slot, uint32_t chunk_bytes) {
+    return static_cast<uint64_t>(static_cast<uint32_t>(slot)) * static_cast<uint32_t>(row_bytes) +
+           chunk_bytes;
+  };
   auto issue = [&](int stage) {
 #pragma unroll
     for (int j = 0; j < NSL; ++j) {
       if constexpr (FP8) {
-        const int64_t off = static_cast<int64_t>(sl[j]) * row_bytes + (lane & 7) * 16;
+        const uint64_t off = row_off(sl[j], (lane & 7) * 16u);
         lds_load16(kb + off, stg + (wave * 16 + 8 * j) * 128);
         lds_load16(vb + off, stg + 8192 + (wave * 16 + 8 * j) * 128);
         rsc[j] = a.kv_scale[sl[j]];
       } else {
         const int r = wave * 16 + 4 * j + (lane >> 4);
         const int c = (lane & 15) ^ mf_row_swz(r);
-        const int64_t off = static_cast<int64_t>(sl[j]) * row_bytes + c * 16;
+        const uint64_t off = row_off(sl[j], c * 16u);
         lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
         lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
       }
@@ -1254,16 +1292,9 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       for (int p = 0; p < 2; ++p) vb[dvb][p] = vbase + mf_swz(vrow0 + 8 * p, 4 * dvb + cl) + 8 * half;
 #pragma unroll
     for (int d2 = 0; d2 < 2; ++d2) {   // two 32-dim value blocks per batch of reads
-      uint32_t ad[16];
-#pragma unroll
-      for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {   // q = 2 * mb + j: keys 16q .. 16q+15 of the tile
-          ad[8 * dd + 2 * q] = vb[2 * d2 + dd][0] + 4096u * q;
-          ad[8 * dd + 2 * q + 1] = vb[2 * d2 + dd][1] + 4096u * q;
-        }
+      // q = 2 * mb + j: keys 16q .. 16q+15 of the tile
       u32x2 rv[16];
-      lds_tr16_x16(rv, ad);
+      lds_tr16_v64(rv, vb[2 * d2][0], vb[2 * d2][1], vb[2 * d2 + 1][0], vb[2 * d2 + 1][1]);
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd)
 #pragma unroll

@@ -176,58 +176,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Eight transposed LDS reads (ds_read_b64_tr_b16) and the wait for them, as one block:
+// Four transposed LDS reads (ds_read_b64_tr_b16) and the wait for them, as one block:
 // the results are valid when it returns. Written as assembly because the compiler orders
 // its own form of this read behind every outstanding global->LDS load (vmcnt(0)), which
 // would wait for the next tile's prefetch in the middle of the current one.
-__device__ __forceinline__ void lds_tr16_x8(u32x2 (&r)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-
-// Sixteen transposed LDS reads and the wait for them (as lds_tr16_x8, one latency for
-// twice the data).
-__device__ __forceinline__ void lds_tr16_x16(u32x2 (&r)[16], const uint32_t (&a)[16]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %17\n\t"
-      "ds_read_b64_tr_b16 %2, %18\n\t"
-      "ds_read_b64_tr_b16 %3, %19\n\t"
-      "ds_read_b64_tr_b16 %4, %20\n\t"
-      "ds_read_b64_tr_b16 %5, %21\n\t"
-      "ds_read_b64_tr_b16 %6, %22\n\t"
-      "ds_read_b64_tr_b16 %7, %23\n\t"
-      "ds_read_b64_tr_b16 %8, %24\n\t"
-      "ds_read_b64_tr_b16 %9, %25\n\t"
-      "ds_read_b64_tr_b16 %10, %26\n\t"
-      "ds_read_b64_tr_b16 %11, %27\n\t"
-      "ds_read_b64_tr_b16 %12, %28\n\t"
-      "ds_read_b64_tr_b16 %13, %29\n\t"
-      "ds_read_b64_tr_b16 %14, %30\n\t"
-      "ds_read_b64_tr_b16 %15, %31\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
-        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]),
-        "v"(a[15])
-      : "memory");
-}
-
-// Four transposed LDS reads and the wait for them (as lds_tr16_x8, fewer registers).
 __device__ __forceinline__ void lds_tr16_x4(u32x2 (&r)[4], const uint32_t (&a)[4]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %4\n\t"
