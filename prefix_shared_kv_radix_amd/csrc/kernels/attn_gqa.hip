@@ -1180,8 +1180,8 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     lds_barrier();
   }
 
-  for (int kt = lo, t = 0; kt < hi; kt += MF_BN, ++t) {
-    const int stage = FP8 ? 0 : t & 1;
+  // one 64-key tile in LDS stage `stage` (the other stage receives the next tile)
+  auto tile_step = [&](int kt, int stage) {
     const bool more = kt + MF_BN < hi;
     if (more) {
       issue(stage ^ 1);
@@ -1199,7 +1199,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
         convert();
         lds_barrier();
       }
-      continue;
+      return;
     }
 
     // S^T per 32-key block. The eight K operands of block 0 are read up front; each is
@@ -1312,6 +1312,18 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       convert();
       lds_barrier();
     }
+  };
+  if constexpr (SEG || FP8) {
+    for (int kt = lo, t = 0; kt < hi; kt += MF_BN, ++t) tile_step(kt, FP8 ? 0 : t & 1);
+  } else {
+    // extend: two tiles per trip, so each copy's LDS stage (and with it the operand
+    // addresses' stage offset) is a constant
+    int kt = lo;
+    for (; kt + MF_BN < hi; kt += 2 * MF_BN) {
+      tile_step(kt, 0);
+      tile_step(kt + MF_BN, 1);
+    }
+    if (kt < hi) tile_step(kt, 0);
   }
 
   l_run += xor32(l_run);
