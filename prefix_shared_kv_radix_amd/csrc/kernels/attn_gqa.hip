@@ -994,8 +994,9 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
 // The sixteen V^T operand reads of two 32-dim value blocks for all 64 keys of a tile, and
 // the wait for them: r[8*dd + 2*q + p] = transposed read at b[2*dd + p] + 4096*q (keys
 // 16q .. 16q+15 lie 16 rows = 4096 bytes apart), the key offsets as immediate offsets of
-// the reads instead of one address add per read. Assembly for the reason given at
-// lds_tr16_x4.
+// the reads instead of one address add per read. Written as assembly: the compiler
+// orders its own form of this read behind every outstanding global->LDS load (vmcnt(0)),
+// which would wait for the next tile's prefetch in the middle of the current one.
 __device__ __forceinline__ void lds_tr16_v64(u32x2 (&r)[16], uint32_t b0, uint32_t b1, uint32_t b2,
                                              uint32_t b3) {
   asm volatile(

@@ -16,10 +16,13 @@
 // run the identical online softmax; then O^T += V^T P^T over the wave's value dims.
 // Per wave that is 72 registers of Q and 128 accumulator registers of O, which fits
 // two waves per SIMD. bf16 tiles are double-buffered in LDS (rows go straight from
-// global memory to LDS); fp8 rows go straight to a staging tile while the one bf16 tile
-// is in use, and are converted into it between tiles. With one
+// global memory to LDS); fp8 rows go straight to one of two staging tiles, and each
+// tile is converted into the free bf16 buffer while the previous tile's values are
+// multiplied. With one
 // chunk per request the block writes the output; with several, partials (o, lse)
 // that combine_kernel merges.
+#include <type_traits>
+
 #include "attn_args.hpp"
 #include "common.hpp"
 
@@ -48,6 +51,23 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
                                    16, 0, 0);
 }
 
+// Four transposed LDS reads at b0 + OFF0, b1 + OFF0, b0 + OFF1, b1 + OFF1 (immediate
+// offsets) and the wait for them. Written as assembly: the compiler orders its own form
+// of this read behind every outstanding global->LDS load (vmcnt(0)), which would wait
+// for the next tile's prefetch in the middle of the current one.
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_tr16_x4_imm(u32x2 (&r)[4], uint32_t b0, uint32_t b1) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(b0), "v"(b1), "n"(OFF0), "n"(OFF1)
+      : "memory");
+}
+
 // Tile layout in LDS (bf16, 36 KB per 32 keys): region A holds dims 0..511 of key r as
 // one 1 KB row, 16-byte chunk c at r*1024 + 16*(c ^ fA(r)); region B holds the rope
 // dims 512..575 as 128-byte rows after it, chunk 64+c at 32768 + r*128 + 16*(c ^ fB(r)).
@@ -62,10 +82,13 @@ __device__ __forceinline__ int fB(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int offA(int r, int c) { return r * 1024 + ((c ^ fA(r)) << 4); }
 __device__ __forceinline__ int offB(int r, int c) { return kRegB + r * 128 + ((c ^ fB(r)) << 4); }
 
+// fp8 staging: two raw tiles (one converting while the next lands), 24 KB each
+constexpr int kStgB = 8 * 3072;
+
 template <bool FP8, int HALF>
-__device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTileB],
-                                         f32x4 (*xs)[4][64], int wave, int b, int lo, int hi,
-                                         int part) {
+__device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTileB], uint8_t *stg,
+                                         float *scl, f32x4 (*xs)[4][64], int wave, int b, int lo,
+                                         int hi, int part) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int hg = wave & 3;
   const int n = lane & 31, h = lane >> 5;
@@ -87,30 +110,44 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
   // ---- tile loads. bf16: region-A row J by wave J % 8 (lane i brings logical chunk
   // i ^ fA(J)); region B by waves 0..3 (lane i: row 8*wave + i/8, chunk i%8 ^ fB(row)).
   // Lane r holds the slot of row r (lanes 32..63 repeat).
-  // fp8: the raw 576-byte rows go straight to a linear staging tile (18 direct loads of
-  // 64 16-byte chunks, spread over the waves), the tile's 32 key scales to a scale
-  // array; once landed, the rows are converted exactly to bf16 (every E4M3 value is a
-  // bf16 value) into the one bf16 tile the matrix code reads, and each key's scale is
-  // applied to its score and its probability instead.
+  // fp8: the raw 576-byte rows go straight to a staging tile, the tile's 32 key scales
+  // to a scale array; once landed, the rows are converted exactly to bf16 (every E4M3
+  // value is a bf16 value) into the bf16 buffer the matrix code reads next, and each
+  // key's scale is applied to its score and its probability instead. Wave w stages rows
+  // 4w .. 4w+3, lane i bringing 16-byte chunks c = i%16 + 16k (k = 0, 1, 2; third-batch
+  // lanes past chunk 35 bring a duplicate) of row 4w + i/16 to staging byte
+  // 3072w + 1024k + 16i, so the thread that converts a chunk is the one that loaded it, at
+  // offsets fixed per thread.
   const uint8_t *kv = static_cast<const uint8_t *>(a.kv);
   const int last = hi - 1;
-  int32_t sl;
-  uint8_t *stg = smem[2];                                        // fp8 staging, 18 KB
-  float *scl = reinterpret_cast<float *>(smem[2] + kBN * kDqk);   // fp8 scales [4][64]
+  int32_t sl, sl_next = 0;
   auto load_slots = [&](int kt) { sl = rtt_row[min(kt + (lane & 31), last)]; };
+  // fp8 loop: the next tile's slots are fetched before this tile's rows are issued (into
+  // their own register, taken over after the end-of-tile wait), so no wait for them can
+  // land behind the row loads; lane offset recomputed here rather than kept live
+  auto load_next_slots = [&](int kt) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    sl_next = rtt_row[min(kt + (ln & 31), last)];
+  };
+  // bf16: rows into buffer `stage`; fp8: tile index `stage` -> staging tile stage & 1,
+  // scale slot stage & 3
   auto issue = [&](int kt, int stage) {
     if (FP8) {
-      for (int i = wave; i < kBN * kDqk / 1024; i += 8) {   // 18 loads of 1 KB
-        const int ch = 64 * i + lane;                        // row ch / 36, chunk ch % 36
-        const int r = ch / 36, c = ch - 36 * r;
-        const int64_t slot = __builtin_amdgcn_ds_bpermute(r << 2, sl);
-        lds_load16(kv + slot * kDqk + c * 16, stg + 1024 * i);
-      }
+      int ln = lane;   // recomputed, not kept live (a spill reload here would wait on loads)
+      asm volatile("" : "+v"(ln));
+      const int r = 4 * wave + (ln >> 4);
+      const int64_t slot = __builtin_amdgcn_ds_bpermute(r << 2, sl);
+      const uint8_t *src = kv + slot * kDqk + (ln & 15) * 16;
+      uint8_t *dst = stg + kStgB * (stage & 1) + 3072 * wave;
+      lds_load16(src, dst);
+      lds_load16(src + 256, dst + 1024);
+      lds_load16(src + ((ln & 15) < 4 ? 512 : 0), dst + 2048);
       if (wave == 0)
         __builtin_amdgcn_global_load_lds(
             a.kv_scale + sl,
             reinterpret_cast<__attribute__((address_space(3))) void *>(
-                reinterpret_cast<uintptr_t>(scl + 64 * stage)),
+                reinterpret_cast<uintptr_t>(scl + 64 * (stage & 3))),
             4, 0, 0);
     } else {
 #pragma unroll
@@ -127,38 +164,46 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
       }
     }
   };
-  // fp8: staged rows -> bf16 tile `dst` (the caller has waited for the loads). Each wave
-  // converts exactly the chunks its own loads brought in, so it needs no barrier before
-  // reusing the staging tile for the next loads, only its own LDS reads done.
-  auto convert = [&](int dst) {
-    for (int ch = tid; ch < kBN * 36; ch += 512) {   // wave-uniform trip count
-      const int r = ch / 36, c = ch - 36 * r;
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(stg + 16 * ch);
-      const u32x4 lo16 = u32x4{fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
-                               fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
-      const u32x4 hi16 = u32x4{fp8x2_to_bf16x2<false>(w[2]), fp8x2_to_bf16x2<true>(w[2]),
-                               fp8x2_to_bf16x2<false>(w[3]), fp8x2_to_bf16x2<true>(w[3])};
-      const int o0 = c < 32 ? offA(r, 2 * c) : offB(r, 2 * (c - 32));
-      const int o1 = c < 32 ? offA(r, 2 * c + 1) : offB(r, 2 * (c - 32) + 1);
-      *reinterpret_cast<u32x4 *>(&smem[dst][o0]) = lo16;
-      *reinterpret_cast<u32x4 *>(&smem[dst][o1]) = hi16;
+  // fp8: one staged chunk (16 E4M3 bytes) -> its two bf16 chunks at o0, o1 of `dst`
+  auto conv_store = [&](const u32x4 &w, uint8_t *dst, int o0, int o1) {
+    const u32x4 lo16 = u32x4{fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                             fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
+    const u32x4 hi16 = u32x4{fp8x2_to_bf16x2<false>(w[2]), fp8x2_to_bf16x2<true>(w[2]),
+                             fp8x2_to_bf16x2<false>(w[3]), fp8x2_to_bf16x2<true>(w[3])};
+    *reinterpret_cast<u32x4 *>(dst + o0) = lo16;
+    *reinterpret_cast<u32x4 *>(dst + o1) = hi16;
+  };
+  // this thread's chunks: row 4*wave + lane/16, fp8 chunk lane%16 + 16k -> bf16 chunks
+  // 2c, 2c+1; the row swizzle only touches the low four chunk bits, so batch k (k < 2)
+  // sits 512k bytes further. The lane-derived offsets are recomputed at each use
+  // (cheap) rather than held in registers across the loop.
+  auto conv_piece = [&](const u32x4 &w, uint8_t *dst, int k) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int cr = 4 * wave + (ln >> 4), i16 = ln & 15;
+    if (k < 2) {
+      conv_store(w, dst, cr * 1024 + (((2 * i16) ^ fA(cr)) << 4) + 512 * k,
+                 cr * 1024 + (((2 * i16 + 1) ^ fA(cr)) << 4) + 512 * k);
+    } else if (i16 < 4) {   // batch 2: rope chunks 32..35
+      conv_store(w, dst, offB(cr, 2 * i16), offB(cr, 2 * i16 + 1));
     }
+  };
+  auto conv_src = [&](int t, int k) {   // staged chunk k of tile t (landed, visible)
+    return *reinterpret_cast<const u32x4 *>(stg + kStgB * (t & 1) + 3072 * wave + 1024 * k +
+                                            16 * lane);
   };
 
   // bf16: tile t+1's loads are in flight while tile t is used (two LDS buffers).
-  // fp8: tile t+2's raw bytes are in flight while tile t is used, and tile t+1, landed,
-  // is converted into the other bf16 buffer at the start of iteration t, overlapping the
-  // other waves' matrix work (key scales: four buffers, tile t in t % 4).
+  // fp8: tile t+2's raw bytes are in flight while tile t is used, and tile t+1 (landed at
+  // the last barrier) is converted into the other bf16 buffer by the same waves, its
+  // pieces placed between tile t's value blocks (key scales: four buffers, tile t in t % 4).
   const int ntiles = hi > lo ? (hi - lo + kBN - 1) / kBN : 0;
   if (ntiles > 0) {
     load_slots(lo);
     issue(lo, 0);
-    if (ntiles > 1) load_slots(lo + kBN);
-    if (FP8) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      convert(0);
-      if (ntiles > 1) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own staging reads done
+    if (ntiles > 1) {
+      load_slots(lo + kBN);
+      if (FP8) {
         issue(lo + kBN, 1);
         if (ntiles > 2) load_slots(lo + 2 * kBN);
       }
@@ -166,18 +211,22 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (FP8 && ntiles > 0) {   // tile 0 into buffer 0
+    uint8_t *d0 = smem[0];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) conv_piece(conv_src(0, k), d0, k);
+    __syncthreads();
+  }
   // V^T operand from the tile: in 16-lane group g, source lane s reads 4 value dims of
   // key row 16j + 4*(g>>1) + (s>>2) (+8 for the second read)
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int kt = lo + t * kBN;
-    if (FP8) {
-      if (t + 1 < ntiles) convert(buf ^ 1);   // tile t+1 (landed at the last barrier)
-      if (t + 2 < ntiles) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue(kt + 2 * kBN, (t + 2) & 3);
-        if (t + 3 < ntiles) load_slots(kt + 3 * kBN);
-      }
+    if (FP8) {   // staging tile t & 1 held tile t, converted during the last iteration
+      // unconditional (clamped: past the end it re-reads the last slot), so no join of
+      // paths forces an early copy of the loaded register (a wait behind the row loads)
+      load_next_slots(kt + 3 * kBN);
+      if (t + 2 < ntiles) issue(kt + 2 * kBN, t + 2);
     } else if (t + 1 < ntiles) {
       issue(kt + kBN, buf ^ 1);
       if (t + 2 < ntiles) load_slots(kt + 2 * kBN);
@@ -196,6 +245,11 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
     const uint8_t *kbase[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) kbase[i] = T + n * 1024 + (((2 * i + h) ^ fA(n)) << 4);
+    // fp8: tile t+1's conversion into the other buffer, in pieces between the value
+    // blocks below (on the last tile it re-converts stale staging bytes into that free
+    // buffer, which nothing reads again)
+    uint8_t *cdst = smem[buf ^ 1];
+    u32x4 cw{};
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int s = 0; s < kHalfQK / 16; ++s) {
@@ -289,26 +343,42 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
         const int r = vrow + 8 * p;
         vb[dm][p] = tb + r * 1024 + (((4 * dm + cl) ^ fA(r)) << 4) + 8 * hb;
       }
-#pragma unroll
-    for (int d = 0; d < kHalfV / 32; ++d) {
-      const uint32_t q256 = 256u * (2 * HALF + (d >> 2));
-      uint32_t ad[4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        ad[2 * j] = vb[d & 3][0] + 16384u * j + q256;
-        ad[2 * j + 1] = vb[d & 3][1] + 16384u * j + q256;
-      }
+    // value block d (compile-time): keys 16j + row at +16384 j, dims at +256 q, both as
+    // immediate offsets of the reads
+    auto pv_block = [&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      constexpr int q256 = 256 * (2 * HALF + (d >> 2));
       u32x2 rv[4];
-      lds_tr16_x4(rv, ad);
+      lds_tr16_x4_imm<q256, 16384 + q256>(rv, vb[d & 3][0], vb[d & 3][1]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const u32x4 w = u32x4{rv[2 * j][0], rv[2 * j][1], rv[2 * j + 1][0], rv[2 * j + 1][1]};
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[j], o[d],
                                                         0, 0, 0);
       }
+    };
+    static_assert(kHalfV / 32 == 8, "eight value blocks per wave");
+    pv_block(std::integral_constant<int, 0>{});
+    if (FP8) cw = conv_src(t + 1, 0);
+    pv_block(std::integral_constant<int, 1>{});
+    pv_block(std::integral_constant<int, 2>{});
+    if (FP8) {
+      conv_piece(cw, cdst, 0);
+      cw = conv_src(t + 1, 1);
     }
+    pv_block(std::integral_constant<int, 3>{});
+    pv_block(std::integral_constant<int, 4>{});
+    if (FP8) {
+      conv_piece(cw, cdst, 1);
+      cw = conv_src(t + 1, 2);
+    }
+    pv_block(std::integral_constant<int, 5>{});
+    pv_block(std::integral_constant<int, 6>{});
+    if (FP8) conv_piece(cw, cdst, 2);
+    pv_block(std::integral_constant<int, 7>{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (FP8) sl = sl_next;
   }
 
   // ---- partial (normalised o, lse in log2 units) or, for a single part, the output;
@@ -347,9 +417,11 @@ __device__ __forceinline__ void mla_body(const MlaArgs &a, uint8_t (*smem)[kTile
 template <bool FP8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_kernel(MlaArgs a) {
-  // bf16 tiles double-buffered; fp8 adds a staging tile and its key scales
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FP8 ? 3 : 2][kTileB];
+  // bf16 tiles double-buffered; fp8 adds two raw staging tiles and four tiles' key scales
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][kTileB];
   __shared__ __attribute__((aligned(16))) f32x4 xs[8][4][64];   // partial scores per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[FP8 ? 2 * kStgB + 4 * 64 * 4 : 16];
+  float *scl = reinterpret_cast<float *>(stage + 2 * kStgB);
 
   // ---- work item: requests in plan order (members of one shared segment are
   // consecutive) spread so that consecutive items land on one XCD; each request's
@@ -364,8 +436,8 @@ void mla_decode_kernel(MlaArgs a) {
   const int lo = split * a.split_chunk;
   const int hi = min(L, lo + a.split_chunk);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) mla_body<FP8, 0>(a, smem, xs, wave, b, lo, hi, split);
-  else mla_body<FP8, 1>(a, smem, xs, wave, b, lo, hi, split);
+  if (wave < 4) mla_body<FP8, 0>(a, smem, stage, scl, xs, wave, b, lo, hi, split);
+  else mla_body<FP8, 1>(a, smem, stage, scl, xs, wave, b, lo, hi, split);
 }
 
 }  // namespace

@@ -176,20 +176,4 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Four transposed LDS reads (ds_read_b64_tr_b16) and the wait for them, as one block:
-// the results are valid when it returns. Written as assembly because the compiler orders
-// its own form of this read behind every outstanding global->LDS load (vmcnt(0)), which
-// would wait for the next tile's prefetch in the middle of the current one.
-__device__ __forceinline__ void lds_tr16_x4(u32x2 (&r)[4], const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-      : "memory");
-}
-
 }  // namespace radix_dev
