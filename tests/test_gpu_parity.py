@@ -396,6 +396,21 @@ def test_mla_splits_and_no_plan(kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_mla_short_contexts(kv):
+    """Contexts of one to three 32-key tiles, and key chunks that are empty, one ragged
+    tile or exactly one tile: every branch of the tile pipeline's start and end (fp8:
+    the staging prologue, the clamped slot fetch past the end, the conversion of a
+    tile that is never read)."""
+    from workloads import mla_groups
+    for seed, args, splits in ((7, (2, 20, 3, 15, 3), (1, 2)),     # 36..38 keys
+                               (8, (2, 40, 2, 30, 3), (1, 4)),     # 71..73 keys: 3 tiles; 4 chunks
+                               (9, (1, 10, 2, 5, 2), (1, 3))):     # 16..17 keys
+        w = mla_groups(seed, kv, *args, q_rows=256)
+        for ns in splits:
+            _run(w, Checker(w), num_splits=ns)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_mla_full_size(kv):
     """Config 5: 256 requests x 4096 context (2048-token prefixes shared by groups of
     32), 32 decode steps: every request at the first and last step."""
