@@ -206,10 +206,9 @@ def test_agent_segment_chunks_bf16(split_keys):
 
 @pytest.mark.parametrize("branch_len,split_keys", [(600, None), (250, None), (600, 192)])
 def test_agent_long_narrow_branches_bf16(branch_len, split_keys):
-    """Narrow shared segments (3 forks x 4 heads = 12 query rows) of 4 to 10 64-key tiles,
-    also cut into 192-key chunks: the chunks whose tiles three loader waves stage through
-    their registers, every step of that rotation (first tiles, tiles 3 and 6 on, ragged
-    last tile) against the oracle."""
+    """Narrow shared segments (3 forks x 4 heads = 12 query rows, one wave of a block's
+    four) of 4 to 10 64-key tiles, also cut into 192-key chunks, with ragged last tiles,
+    against the oracle."""
     w = agent_branch(5, gqa128_shape(), 2, 128, 3, branch_len, 3, 4, q_rows=4096)
     _run(w, Checker(w, extend_sample=2), split_keys=split_keys)
 
