@@ -430,21 +430,24 @@ def cpu_baseline(w, seconds):
 
 
 def read_bandwidth(mib=1024, reps=10):
-    """Device read rate of a plain reduction over `mib` MiB of fp32 (bytes read per second,
-    median of `reps` event-timed sums): the read-only ceiling for gather-heavy kernels."""
+    """Device read rate of the library's streaming read probe (radix_probe_read) over
+    `mib` MiB (bytes read per second, median of `reps` event-timed passes on the current
+    stream): the practical read-only ceiling beside the nominal 8 TB/s."""
     import torch
+    from prefix_shared_kv_radix_amd import _lib
     n = (mib << 20) // 4
-    x = torch.ones(n, dtype=torch.float32, device="cuda")
-    x.sum()
+    x = torch.ones(n, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    _lib.probe_read(x, sink)
     times = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        x.sum()
+        _lib.probe_read(x, sink)
         b.record()
         b.synchronize()
         times.append(a.elapsed_time(b) / 1e3)
-    del x
+    del x, sink
     return 4.0 * n / float(np.median(times)) / 1e9
 
 

@@ -445,6 +445,18 @@ radix_status radix_fence_wait(radix_fence *fence);
 void radix_fence_destroy(radix_fence *fence);
 
 /* ======================================================================
+ * Practical HBM read ceiling for measurement tools (not part of the attention
+ * path): reads `bytes` (a positive multiple of 16) from the device buffer `buf`
+ * (16-byte aligned) once, with every lane keeping eight non-temporal 16-byte loads in
+ * flight, on `stream`. `sink` is a device array of at least 8192 uint32 that the kernel
+ * writes only when the XOR of everything read equals a fixed constant; its
+ * contents are not meaningful. Time it with events on the same stream.
+ * Errors: RADIX_E_INVAL for a missing pointer, a misaligned buffer or a bad size;
+ * a launch failure as the HIP status.
+ * ====================================================================== */
+radix_status radix_probe_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
+/* ======================================================================
  * Kernel timing for measurement tools. While enabled, every kernel the
  * attention calls launch is bracketed by two HIP events recorded on the
  * launch stream (up to `capacity` launches; later ones are not recorded).

@@ -99,6 +99,7 @@ _SIGS = {
                                         _i64p, _i64p, _i64p]),
     "radix_req_finish_batch": (C.c_int, [_vp, _i32p, _i64p, _i32p, C.c_int64, _i64p, _i64p,
                                          C.c_int64, _i64p]),
+    "radix_probe_read": (C.c_int, [_vp, C.c_int64, _vp, _vp]),
     "radix_fence_create": (C.c_int, [C.POINTER(_vp)]),
     "radix_fence_record": (C.c_int, [_vp, _vp]),
     "radix_fence_wait": (C.c_int, [_vp]),
@@ -523,6 +524,15 @@ def attn_decode(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token, 
         _ptr(new_slots), _ptr(req_to_token), int(req_to_token.shape[1]), _ptr(req_rows),
         _ptr(seq_lens), int(batch), int(max_seq_len), None if plan is None else C.byref(plan),
         int(num_splits), _ptr(out), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def probe_read(buf, sink, stream=None):
+    """Read the device tensor `buf` once (radix_probe_read); `sink`: >= 8192 int32 on the
+    device."""
+    if buf.numel() * buf.element_size() % 16 or sink.numel() < 8192:
+        raise ValueError("probe_read: buffer bytes must be a multiple of 16, sink >= 8192 words")
+    _check(load().radix_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                   _stream(stream)))
 
 
 def attn_decode_noalloc(shape, kv, q, k_new, v_new, scale_new, new_slots, req_to_token, req_rows,

@@ -274,6 +274,34 @@ __global__ void zero_words_kernel(uint32_t *p, int64_t n) {
     p[i] = 0u;
 }
 
+// Streaming read of n16 16-byte words, eight non-temporal loads in flight per lane (the
+// fastest simple read pattern measured: ≈ 6.2 TB/s, against ≈ 5.4 with default-policy
+// loads); the XOR of everything read reaches memory only if it equals a fixed constant,
+// so the loads stay.
+constexpr unsigned kProbeBlocks = 8192;
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4 *p, int64_t n16,
+                                                         uint32_t *sink) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      typedef unsigned u4 __attribute__((ext_vector_type(4)));
+      const u4 w = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(p + i + k * stride));
+      v[k] = uint4{w[0], w[1], w[2], w[3]};
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices] = {};
@@ -621,6 +649,15 @@ radix_status radix_attn_decode_noalloc(const radix_attn_shape *shape, const radi
 }
 
 size_t radix_attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+radix_status radix_probe_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+  REQUIRE(buf && sink, "read probe: missing buffer or sink");
+  REQUIRE(bytes > 0 && bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(buf) & 15) == 0,
+          "read probe: buffer must be 16-byte aligned, a positive multiple of 16 bytes");
+  read_probe_kernel<<<dim3(kProbeBlocks), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4 *>(buf), bytes / 16, sink);
+  return hip_status(hipGetLastError(), "read probe launch");
+}
 
 radix_status radix_fence_create(radix_fence **out) {
   REQUIRE(out, "null output pointer");

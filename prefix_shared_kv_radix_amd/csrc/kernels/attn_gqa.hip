@@ -985,10 +985,13 @@ __device__ __forceinline__ int mf_row_swz(int r) { return ((r & 3) << 2) | ((r >
 __device__ __forceinline__ int mf_swz(int r, int c) { return r * 256 + ((c ^ mf_row_swz(r)) << 4); }
 
 
+// Direct global -> LDS load of 16 bytes per lane; NT = 1: non-temporal (cache-policy
+// bit 2 of the instruction, `nt`), for rows that no other block reads.
+template <int NT = 0>
 __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
   __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void *>(
                                           reinterpret_cast<uintptr_t>(lds_base)),
-                                   16, 0, 0);
+                                   16, 0, NT ? 2 : 0);
 }
 
 // The sixteen V^T operand reads of two 32-dim value blocks for all 64 keys of a tile, and
@@ -1134,20 +1137,34 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     return static_cast<uint64_t>(static_cast<uint32_t>(slot)) * static_cast<uint32_t>(row_bytes) +
            chunk_bytes;
   };
+  // a shared-segment chunk with a single tile of rows is the only reader of its K/V
+  // rows: those loads go non-temporal (agent decode step ≈ 7 % faster); chunks read by
+  // several row tiles, and extend tiles, keep them in the XCD's L2 for the other tiles
+  const bool nt_rows = SEG && nrows <= MF_BM;   // block-uniform
   auto issue = [&](int stage) {
 #pragma unroll
     for (int j = 0; j < NSL; ++j) {
       if constexpr (FP8) {
         const uint64_t off = row_off(sl[j], (lane & 7) * 16u);
-        lds_load16(kb + off, stg + (wave * 16 + 8 * j) * 128);
-        lds_load16(vb + off, stg + 8192 + (wave * 16 + 8 * j) * 128);
+        if (nt_rows) {
+          lds_load16<1>(kb + off, stg + (wave * 16 + 8 * j) * 128);
+          lds_load16<1>(vb + off, stg + 8192 + (wave * 16 + 8 * j) * 128);
+        } else {
+          lds_load16(kb + off, stg + (wave * 16 + 8 * j) * 128);
+          lds_load16(vb + off, stg + 8192 + (wave * 16 + 8 * j) * 128);
+        }
         rsc[j] = a.kv_scale[sl[j]];
       } else {
         const int r = wave * 16 + 4 * j + (lane >> 4);
         const int c = (lane & 15) ^ mf_row_swz(r);
         const uint64_t off = row_off(sl[j], c * 16u);
-        lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
-        lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
+        if (nt_rows) {
+          lds_load16<1>(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
+          lds_load16<1>(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
+        } else {
+          lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
+          lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
+        }
       }
     }
   };

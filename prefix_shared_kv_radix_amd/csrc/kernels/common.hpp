@@ -90,7 +90,10 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
 
 // Loads whose completion the compiler does not track: the caller waits for them with
 // an explicit s_waitcnt that names the destination registers (see the private-tail
-// ring). Nothing may read or copy the destination before that wait.
+// ring). Nothing may read or copy the destination before that wait. The K/V row loads
+// (8 and 16 bytes) are non-temporal: a private tail's rows are read once per step, and
+// streaming them past the caches' retention reads about 5 % faster (measured on the
+// decode steps); slots and scales keep the default policy.
 __device__ __forceinline__ int32_t ld_async4(const int32_t *p) {
   int32_t v;
   asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
@@ -103,13 +106,13 @@ __device__ __forceinline__ float ld_async4f(const float *p) {
 }
 __device__ __forceinline__ u32x2 ld_async8(const void *p) {
   u32x2 v;
-  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  asm volatile("global_load_dwordx2 %0, %1, off nt" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
 template <int OFF>
 __device__ __forceinline__ u32x4 ld_async16(const void *p) {
   u32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2 nt" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
   return v;
 }
 
