@@ -1258,42 +1258,50 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
           st[mb][i] = (key < hi && key <= qpos) ? st[mb][i] : -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // P against the running maximum as it stands, packed to bf16 for the PV product, and
+    // its fp32 row sum (two chains). The maximum is raised, and the accumulators
+    // rescaled, only when some lane's probabilities in this tile sum past 2^8 or
+    // overflow (the first tile, whose maximum is still the start value): every p is at
+    // most that sum, so p <= 2^8 whenever the tile is kept.
+    bf16x8 pb[2][2];
+    float rs;
+    auto exp_pack = [&]() {
+      float ra = 0.f, rb = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(st[mb][i], st[mb][i + 1]));
-    mx = fmaxf(mx, xor32(mx)) * sc;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
+        for (int j = 0; j < 2; ++j) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 8 * j + 2 * e;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(st[mb][i], sc, -m_run));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(st[mb][i + 1], sc, -m_run));
+            w[e] = pack2bf(p0, p1);
+            ra += p0;
+            rb += p1;
+          }
+          pb[mb][j] = __builtin_bit_cast(bf16x8, w);
+        }
+      rs = ra + rb;
+    };
+    exp_pack();
+    if (__builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(st[mb][i], st[mb][i + 1]));
+      mx = fmaxf(mx, xor32(mx)) * sc;
       const float mn = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d) o[d] *= alpha;
+      exp_pack();
     }
-    float rs = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[mb][i], sc, -m_run));
-        st[mb][i] = p;
-        rs += p;
-      }
     l_run += rs;   // this half's keys; the halves are added once, after the loop
-
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack2bf(st[mb][8 * j + 2 * e], st[mb][8 * j + 2 * e + 1]);
-        pb[mb][j] = __builtin_bit_cast(bf16x8, w);
-      }
     // V^T operand: in each 16-lane group g, source lane s reads 4 dims of key row
     // base + 4*(g>>1) + (s>>2) (+8 for the second read); the transpose hands lane s the
     // 4 keys of value dim 16*(g&1) + s of the 32-dim block.
