@@ -25,6 +25,7 @@
 //                     read of the segment's KV serves every member).
 //   combine_kernel    merges per-request partial results.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "attn_args.hpp"
@@ -994,36 +995,37 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds_base) {
                                    16, 0, NT ? 2 : 0);
 }
 
-// The sixteen V^T operand reads of two 32-dim value blocks for all 64 keys of a tile, and
-// the wait for them: r[8*dd + 2*q + p] = transposed read at b[2*dd + p] + 4096*q (keys
-// 16q .. 16q+15 lie 16 rows = 4096 bytes apart), the key offsets as immediate offsets of
-// the reads instead of one address add per read. Written as assembly: the compiler
-// orders its own form of this read behind every outstanding global->LDS load (vmcnt(0)),
-// which would wait for the next tile's prefetch in the middle of the current one.
-__device__ __forceinline__ void lds_tr16_v64(u32x2 (&r)[16], uint32_t b0, uint32_t b1, uint32_t b2,
-                                             uint32_t b3) {
+// The sixteen V^T operand reads of one 32-key block for all four 32-dim value blocks, and
+// the wait for them: r[4*dvb + 2*qq + p] = transposed read at b[dvb][p] + OFF + 4096*qq
+// (keys OFF/256 + 16*qq .. +15; key rows are 256 bytes apart), the key offsets as
+// immediate offsets of the reads. Written as assembly: the compiler orders its own form of
+// this read behind every outstanding global->LDS load (vmcnt(0)), which would wait for the
+// next tile's prefetch in the middle of the current one.
+template <int OFF>
+__device__ __forceinline__ void lds_tr16_k32(u32x2 (&r)[16], const uint32_t (&b)[4][2]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %17\n\t"
-      "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %4, %16 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %5, %17 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %6, %16 offset:12288\n\t"
-      "ds_read_b64_tr_b16 %7, %17 offset:12288\n\t"
-      "ds_read_b64_tr_b16 %8, %18\n\t"
-      "ds_read_b64_tr_b16 %9, %19\n\t"
-      "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %11, %19 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %12, %18 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %13, %19 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %14, %18 offset:12288\n\t"
-      "ds_read_b64_tr_b16 %15, %19 offset:12288\n\t"
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %10, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %13, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
         "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
         "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+      : "v"(b[0][0]), "v"(b[0][1]), "v"(b[1][0]), "v"(b[1][1]), "v"(b[2][0]), "v"(b[2][1]),
+        "v"(b[3][0]), "v"(b[3][1]), "n"(OFF), "n"(OFF + 4096)
       : "memory");
 }
 
@@ -1198,100 +1200,47 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     lds_barrier();
   }
 
-  // one 64-key tile in LDS stage `stage` (the other stage receives the next tile)
-  auto tile_step = [&](int kt, int stage) {
-    const bool more = kt + MF_BN < hi;
-    if (more) {
-      issue(stage ^ 1);
-      if (kt + 2 * MF_BN < hi) load_slots(kt + 2 * MF_BN);
+  // ---- one 64-key tile, as two 32-key blocks mb = 0, 1 whose phases overlap: block 1's
+  // scores are formed on the matrix cores while block 0's softmax runs on the vector
+  // ALUs, and block 0's PV products while block 1's softmax runs (the two interleaved
+  // instruction by instruction), so a wave keeps both units busy by itself.
+  // Ragged or causal-diagonal block: keys past the range or past the row's position -> -inf.
+  auto mask = [&](f32x16 &sb, int kb0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb0 + 8 * (i >> 2) + 4 * h + (i & 3);
+      sb[i] = (key < hi && key <= qpos) ? sb[i] : -INFINITY;
     }
-    const uint8_t *Kt = smem[stage][0];
-    const uint8_t *Vt = smem[stage][1];
-    // a wave whose 32 rows are all past the block's rows (small shared segments) only
-    // loads (and, fp8, converts) its share of each tile and keeps the barriers, leaving
-    // the SIMD to others
-    if (!wave_active) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (FP8 && more) {
-        convert();
-        lds_barrier();
+  };
+  // P of block mb against the running maximum as it stands, packed to bf16 for the PV
+  // product, and its fp32 row sum (two chains; this lane's 16 keys). The maximum is
+  // raised, and the accumulators rescaled, only when some lane's probabilities in the
+  // block sum past 2^8 or overflow (the first block, whose maximum is still the start
+  // value): every p is at most that sum, so p <= 2^8 whenever the block is kept.
+  bf16x8 pb[2][2];
+  auto exp_pack = [&](const f32x16 &sb, int mb) {
+    float ra = 0.f, rb = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 8 * j + 2 * e;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[i], sc, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[i + 1], sc, -m_run));
+        w[e] = pack2bf(p0, p1);
+        ra += p0;
+        rb += p1;
       }
-      return;
+      pb[mb][j] = __builtin_bit_cast(bf16x8, w);
     }
-
-    // S^T per 32-key block. The eight K operands of block 0 are read up front; each is
-    // refilled with block 1's operand right after the MFMA that used it, so the reads
-    // overlap the MFMAs instead of one LDS latency being exposed per MFMA.
-    f32x16 st[2];
-    {
-      bf16x8 ka[MF_D / 16];
-#pragma unroll
-      for (int s = 0; s < MF_D / 16; ++s)
-        ka[s] = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(n, 2 * s + h));
-      st[0] = f32x16{};
-      st[1] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < MF_D / 16; ++s) {
-        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st[0], 0, 0, 0);
-        ka[s] = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(32 + n, 2 * s + h));
-      }
-#pragma unroll
-      for (int s = 0; s < MF_D / 16; ++s)
-        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st[1], 0, 0, 0);
-      // keep that order through scheduling: 8 LDS reads, then (MFMA, LDS read) x 8,
-      // then 8 MFMAs (masks: 0x100 LDS read, 0x008 MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int s = 0; s < MF_D / 16; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-    if (kt + MF_BN > hi || kt + MF_BN - 1 > wave_q0) {   // (wave-uniform) ragged or diagonal tile
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt + mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          st[mb][i] = (key < hi && key <= qpos) ? st[mb][i] : -INFINITY;
-        }
-    }
-    // P against the running maximum as it stands, packed to bf16 for the PV product, and
-    // its fp32 row sum (two chains). The maximum is raised, and the accumulators
-    // rescaled, only when some lane's probabilities in this tile sum past 2^8 or
-    // overflow (the first tile, whose maximum is still the start value): every p is at
-    // most that sum, so p <= 2^8 whenever the tile is kept.
-    bf16x8 pb[2][2];
-    float rs;
-    auto exp_pack = [&]() {
-      float ra = 0.f, rb = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 8 * j + 2 * e;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(st[mb][i], sc, -m_run));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(st[mb][i + 1], sc, -m_run));
-            w[e] = pack2bf(p0, p1);
-            ra += p0;
-            rb += p1;
-          }
-          pb[mb][j] = __builtin_bit_cast(bf16x8, w);
-        }
-      rs = ra + rb;
-    };
-    exp_pack();
+    return ra + rb;
+  };
+  auto softmax_tail = [&](const f32x16 &sb, int mb, float rs) {
     if (__builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(st[mb][i], st[mb][i + 1]));
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sb[i], sb[i + 1]));
       mx = fmaxf(mx, xor32(mx)) * sc;
       const float mn = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
@@ -1299,39 +1248,136 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d) o[d] *= alpha;
-      exp_pack();
+      rs = exp_pack(sb, mb);
     }
-    l_run += rs;   // this half's keys; the halves are added once, after the loop
-    // V^T operand: in each 16-lane group g, source lane s reads 4 dims of key row
-    // base + 4*(g>>1) + (s>>2) (+8 for the second read); the transpose hands lane s the
-    // 4 keys of value dim 16*(g&1) + s of the 32-dim block.
-    const int g = lane >> 4, s16 = lane & 15;
-    const int vrow0 = 4 * (g >> 1) + (s16 >> 2);
+    l_run += rs;   // this half-wave's keys; the halves are added once, after the loop
+  };
+  // V^T operand: in each 16-lane group g, source lane s reads 4 dims of key row
+  // base + 4*(g>>1) + (s>>2) (+8 for the second read); the transpose hands lane s the
+  // 4 keys of value dim 16*(g&1) + s of the 32-dim block. Chunk of value block dvb =
+  // 4*dvb + cl, and rows 16q + x (x < 16) share x's swizzle: one lane base per (dvb, row
+  // vrow0 or vrow0 + 8), keys 16q as constant offsets of the reads.
+  const int vg = lane >> 4, vs16 = lane & 15;
+  const int vrow0 = 4 * (vg >> 1) + (vs16 >> 2);
+  const int vcl = 2 * (vg & 1) + ((vs16 & 3) >> 1), vhalf = vs16 & 1;
+  auto v_bases = [&](const uint8_t *Vt, uint32_t (&vbs)[4][2]) {
     const uint32_t vbase = lds_addr(Vt);
-    // chunk of value block dvb = 4*dvb + cl, and rows 16q + x (x < 16) share x's swizzle:
-    // one lane base per (dvb, row vrow0 or vrow0 + 8), keys 16q as constant offsets
-    const int cl = 2 * (g & 1) + ((s16 & 3) >> 1), half = s16 & 1;
-    uint32_t vb[4][2];
 #pragma unroll
     for (int dvb = 0; dvb < 4; ++dvb)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) vb[dvb][p] = vbase + mf_swz(vrow0 + 8 * p, 4 * dvb + cl) + 8 * half;
+      for (int p = 0; p < 2; ++p) vbs[dvb][p] = vbase + mf_swz(vrow0 + 8 * p, 4 * dvb + vcl) + 8 * vhalf;
+  };
+  // O^T += V^T P^T over block mb's keys (16-key steps q = 2mb, 2mb + 1): rv[4*dvb + 2*qq + p]
+  // holds the transposed read at base (dvb, p), keys 16*(2mb + qq)
+  auto pv = [&](const u32x2 (&rv)[16], int mb) {
 #pragma unroll
-    for (int d2 = 0; d2 < 2; ++d2) {   // two 32-dim value blocks per batch of reads
-      // q = 2 * mb + j: keys 16q .. 16q+15 of the tile
-      u32x2 rv[16];
-      lds_tr16_v64(rv, vb[2 * d2][0], vb[2 * d2][1], vb[2 * d2 + 1][0], vb[2 * d2 + 1][1]);
+    for (int dvb = 0; dvb < 4; ++dvb)
 #pragma unroll
-      for (int dd = 0; dd < 2; ++dd)
+      for (int qq = 0; qq < 2; ++qq) {
+        const u32x4 w = u32x4{rv[4 * dvb + 2 * qq][0], rv[4 * dvb + 2 * qq][1],
+                              rv[4 * dvb + 2 * qq + 1][0], rv[4 * dvb + 2 * qq + 1][1]};
+        o[dvb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[mb][qq],
+                                                         o[dvb], 0, 0, 0);
+      }
+  };
+
+  // the matrix and softmax work of one 64-key tile in LDS stage `stage`; DIAG: ragged or
+  // causal-diagonal tile (a compile-time variant, so each body is one straight block in
+  // which the scheduler can interleave the two units' instructions)
+  auto tile_body = [&](auto DIAG, int kt, int stage) {
+    // DIAG: std::true_type / std::false_type, or a run-time bool (fp8 extend, whose
+    // conversion pass leaves no registers for two copies of the body)
+    auto maybe_mask = [&](f32x16 &sb, int kb0) {
+      if constexpr (std::is_same<decltype(DIAG), bool>::value) {
+        if (DIAG) mask(sb, kb0);
+      } else if constexpr (decltype(DIAG)::value) {
+        mask(sb, kb0);
+      }
+    };
+    const uint8_t *Kt = smem[stage][0];
+    uint32_t vbs[4][2];
+    v_bases(smem[stage][1], vbs);
+    f32x16 st0, st1;
+    bf16x8 ka[MF_D / 16];
+    // S^T of block 0; each K operand of block 0 is refilled with block 1's right after
+    // the MFMA that used it, so the reads overlap the MFMAs
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int dvb = 2 * d2 + dd;
-          const u32x4 w = u32x4{rv[8 * dd + 2 * q][0], rv[8 * dd + 2 * q][1],
-                                rv[8 * dd + 2 * q + 1][0], rv[8 * dd + 2 * q + 1][1]};
-          o[dvb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
-                                                           pb[q >> 1][q & 1], o[dvb], 0, 0, 0);
-        }
+    for (int s = 0; s < MF_D / 16; ++s)
+      ka[s] = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(n, 2 * s + h));
+    st0 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < MF_D / 16; ++s) {
+      st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st0, 0, 0, 0);
+      ka[s] = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(32 + n, 2 * s + h));
     }
+    // block 1's scores on the matrix cores, block 0's softmax on the vector ALUs
+    st1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < MF_D / 16; ++s)
+      st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st1, 0, 0, 0);
+    if constexpr (FP8 && !SEG) {
+      // fp8 extend (its mask test is a branch): the two blocks one after the other
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int s = 0; s < MF_D / 16; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      maybe_mask(st0, kt);
+      maybe_mask(st1, kt + 32);
+      softmax_tail(st0, 0, exp_pack(st0, 0));
+      softmax_tail(st1, 1, exp_pack(st1, 1));
+      u32x2 rv[16];
+      lds_tr16_k32<0>(rv, vbs);
+      pv(rv, 0);
+      lds_tr16_k32<8192>(rv, vbs);
+      pv(rv, 1);
+      return;
+    }
+    maybe_mask(st0, kt);
+    float rs = exp_pack(st0, 0);
+    // 8 LDS reads, (MFMA, LDS read) x 8, then (MFMA, 7 vector instructions) x 8
+    // (masks: 0x100 LDS read, 0x008 MFMA, 0x002 VALU)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int s = 0; s < MF_D / 16; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < MF_D / 16; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+    softmax_tail(st0, 0, rs);
+    // V^T operands of keys 0..31 and 32..63
+    u32x2 rv0[16], rv1[16];
+    lds_tr16_k32<0>(rv0, vbs);
+    lds_tr16_k32<8192>(rv1, vbs);
+    // block 0's PV products on the matrix cores, block 1's softmax on the vector ALUs
+    pv(rv0, 0);
+    maybe_mask(st1, kt + 32);
+    rs = exp_pack(st1, 1);
+#pragma unroll
+    for (int s = 0; s < MF_D / 16; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+    softmax_tail(st1, 1, rs);
+    pv(rv1, 1);
+  };
+  // one 64-key tile in LDS stage `stage` (the other stage receives the next tile)
+  auto tile_step = [&](auto DIAG, int kt, int stage) {
+    const bool more = kt + MF_BN < hi;
+    if (more) {
+      issue(stage ^ 1);
+      if (kt + 2 * MF_BN < hi) load_slots(kt + 2 * MF_BN);
+    }
+    // a wave whose 32 rows are all past the block's rows (small shared segments) only
+    // loads (and, fp8, converts) its share of each tile and keeps the barriers, leaving
+    // the SIMD to others
+    if (wave_active) tile_body(DIAG, kt, stage);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (FP8 && more) {   // the next tile's bytes have landed and nobody reads this tile now
@@ -1339,17 +1385,30 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       lds_barrier();
     }
   };
-  if constexpr (SEG || FP8) {
-    for (int kt = lo, t = 0; kt < hi; kt += MF_BN, ++t) tile_step(kt, FP8 ? 0 : t & 1);
+  // Tiles starting at or before `lim` are whole and wholly at or before this wave's first
+  // query position, so they need no mask; the ragged or causal-diagonal ones come last.
+  // Waves differ in where they switch to the masked body, but all run the same tiles and
+  // barriers.
+  const int lim = min(hi - MF_BN, wave_q0 - (MF_BN - 1));
+  if constexpr (SEG) {
+    int kt = lo, t = 0;
+    for (; kt <= lim; kt += MF_BN, ++t) tile_step(std::false_type{}, kt, FP8 ? 0 : t & 1);
+    for (; kt < hi; kt += MF_BN, ++t) tile_step(std::true_type{}, kt, FP8 ? 0 : t & 1);
+  } else if constexpr (FP8) {
+    for (int kt = lo; kt < hi; kt += MF_BN) tile_step(kt > lim, kt, 0);
   } else {
     // extend: two tiles per trip, so each copy's LDS stage (and with it the operand
     // addresses' stage offset) is a constant
     int kt = lo;
-    for (; kt + MF_BN < hi; kt += 2 * MF_BN) {
-      tile_step(kt, 0);
-      tile_step(kt + MF_BN, 1);
+    for (; kt + MF_BN <= lim; kt += 2 * MF_BN) {
+      tile_step(std::false_type{}, kt, 0);
+      tile_step(std::false_type{}, kt + MF_BN, 1);
     }
-    if (kt < hi) tile_step(kt, 0);
+    for (; kt + MF_BN < hi; kt += 2 * MF_BN) {
+      tile_step(std::true_type{}, kt, 0);
+      tile_step(std::true_type{}, kt + MF_BN, 1);
+    }
+    if (kt < hi) tile_step(std::true_type{}, kt, 0);
   }
 
   l_run += xor32(l_run);
