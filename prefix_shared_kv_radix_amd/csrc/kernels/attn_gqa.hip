@@ -1497,14 +1497,16 @@ __host__ __device__ __forceinline__ int seg_block_count(int tiles, int groups) {
   return 8 * tiles * ((groups + 7) / 8);
 }
 
-// extend: logical block -> (tile, request, kvh), tile fastest
+// extend: logical block -> (tile, request, kvh), tile fastest and in decreasing order:
+// a causal request's last row tiles have the most keys, and dispatching them first keeps
+// the launch from ending on its longest blocks
 template <int G, bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
   const int nblocks = tiles * items * a.Hkv;
   const int lb = xcd_logical(blockIdx.x, nblocks);
   if (lb >= nblocks) return;
-  mfma_body<G, false, FP8>(a, lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
+  mfma_body<G, false, FP8>(a, tiles - 1 - lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
 }
 
 // One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
