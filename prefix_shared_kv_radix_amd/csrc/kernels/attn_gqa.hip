@@ -1039,9 +1039,12 @@ __device__ __forceinline__ void lds_tr16_k32(u32x2 (&r)[16], const uint32_t (&b)
 // K/V tiles go global -> LDS with direct 16-byte loads, two stages: tile t+1 is in flight
 // while tile t is multiplied. Query rows are a request's new tokens x heads (extend,
 // causal) or the members of a shared radix segment x heads (decode partials).
+// Shared-segment chunks of at most this many keys stage their slot list in LDS.
+constexpr int kSegSlotCap = 2048;
+
 template <int G, bool SEG, bool FP8>
 __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item, int kvh,
-                                          uint8_t (*smem)[2][MF_TILE]) {
+                                          uint8_t (*smem)[2][MF_TILE], int32_t *slot_lds = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
@@ -1187,18 +1190,6 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       }
     }
   };
-
-  if (lo < hi) {
-    load_slots(lo);
-    issue(0);
-    if (lo + MF_BN < hi) load_slots(lo + MF_BN);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (FP8 && lo < hi) {
-    convert();
-    lds_barrier();
-  }
 
   // ---- one 64-key tile, as two 32-key blocks mb = 0, 1 whose phases overlap: block 1's
   // scores are formed on the matrix cores while block 0's softmax runs on the vector
@@ -1390,6 +1381,91 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   // Waves differ in where they switch to the masked body, but all run the same tiles and
   // barriers.
   const int lim = min(hi - MF_BN, wave_q0 - (MF_BN - 1));
+  bool ring = false;
+  if constexpr (SEG && !FP8)   // (uniform) chunks of one row tile
+    ring = slot_lds != nullptr && hi - lo <= kSegSlotCap && nrows <= MF_BM;
+  if (ring) {
+    // Shared-segment chunk of one row tile, bf16: its tiles wait on memory, not on the
+    // matrix cores, so the chunk runs as 32-key tiles through a four-deep ring (three
+    // tiles, 48 KB, in flight instead of one 64-key tile). Its slot list is staged in LDS
+    // first, so the loop issues only tile loads and waits for exact counts of them.
+    // (Chunks of several row tiles keep the 64-key tiles, whose two blocks overlap their
+    // matrix and softmax work.)
+    const int n32 = (hi - lo + 31) / 32;
+    for (int c = wave; c < (n32 + 1) / 2; c += 4)   // 64 entries per wave instruction
+      __builtin_amdgcn_global_load_lds(rtt_row + min(lo + 64 * c + lane, last),
+                                       reinterpret_cast<__attribute__((address_space(3))) void *>(
+                                           reinterpret_cast<uintptr_t>(slot_lds + 64 * c)),
+                                       4, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint8_t *ring_lds = smem[0][0];   // stage s: K at 16 KB * s, V 8 KB after it
+    auto issue32 = [&](int t, int stage) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // lane i lands at byte 16*i of the 4-row group (row +i/16, physical chunk i%16)
+        const int r = wave * 8 + 4 * j + (lane >> 4);
+        const uint64_t off = row_off(slot_lds[32 * t + r], ((lane & 15) ^ mf_row_swz(r)) * 16u);
+        uint8_t *dst = ring_lds + 16384 * stage + (wave * 8 + 4 * j) * 256;
+        if (nt_rows) {
+          lds_load16<1>(kb + off, dst);
+          lds_load16<1>(vb + off, dst + 8192);
+        } else {
+          lds_load16(kb + off, dst);
+          lds_load16(vb + off, dst + 8192);
+        }
+      }
+    };
+    // waits until at most n later tiles' loads (4 per lane each) are outstanding
+    auto wait_tiles = [&](int n) {
+      if (n >= 2)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (n == 1)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    // (barriers that leave later tiles' loads in flight: __syncthreads() would wait for
+    // them; a tile's own loads are waited for explicitly first)
+    for (int t = 0; t < 3 && t < n32; ++t) issue32(t, t);
+    wait_tiles(min(n32, 3) - 1);
+    lds_barrier();
+    for (int t = 0; t < n32; ++t) {
+      if (t + 3 < n32) issue32(t + 3, (t + 3) & 3);
+      if (wave_active) {
+        const int kt = lo + 32 * t;
+        const uint8_t *Kt = ring_lds + 16384 * (t & 3);
+        bf16x8 ka[MF_D / 16];
+#pragma unroll
+        for (int s = 0; s < MF_D / 16; ++s)
+          ka[s] = *reinterpret_cast<const bf16x8 *>(Kt + mf_swz(n, 2 * s + h));
+        f32x16 st0 = f32x16{};
+#pragma unroll
+        for (int s = 0; s < MF_D / 16; ++s)
+          st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qb[s], st0, 0, 0, 0);
+        if (kt + 32 > hi) mask(st0, kt);   // (uniform) ragged last tile
+        softmax_tail(st0, 0, exp_pack(st0, 0));
+        uint32_t vbs[4][2];
+        v_bases(Kt + 8192, vbs);
+        u32x2 rv[16];
+        lds_tr16_k32<0>(rv, vbs);
+        pv(rv, 0);
+      }
+      wait_tiles(min(n32 - 1, t + 3) - (t + 1));   // tile t+1 has landed
+      lds_barrier();
+    }
+  } else {
+  if (lo < hi) {
+    load_slots(lo);
+    issue(0);
+    if (lo + MF_BN < hi) load_slots(lo + MF_BN);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (FP8 && lo < hi) {
+    convert();
+    lds_barrier();
+  }
   if constexpr (SEG) {
     int kt = lo, t = 0;
     for (; kt <= lim; kt += MF_BN, ++t) tile_step(std::false_type{}, kt, FP8 ? 0 : t & 1);
@@ -1409,6 +1485,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
       tile_step(std::true_type{}, kt + MF_BN, 1);
     }
     if (kt < hi) tile_step(std::true_type{}, kt, 0);
+  }
   }
 
   l_run += xor32(l_run);
@@ -1516,6 +1593,7 @@ template <int G, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int tiles, int seg_items,
                                                              int n_items, int nsplit) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];
+  __shared__ int32_t slot_lds[kSegSlotCap];
   const int groups = seg_items * a.Hkv;   // (chunk, KV head) pairs, `tiles` blocks each
   const int seg_blocks = seg_block_count(tiles, groups);
   if (static_cast<int>(blockIdx.x) < seg_blocks) {
@@ -1526,7 +1604,7 @@ __global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int ti
     const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
     const int g = xcd + 8 * (k / tiles);
     if (g >= groups) return;
-    mfma_body<G, true, FP8>(a, k % tiles, g / a.Hkv, g % a.Hkv, smem);
+    mfma_body<G, true, FP8>(a, k % tiles, g / a.Hkv, g % a.Hkv, smem, FP8 ? nullptr : slot_lds);
   } else {
     tail_bf16_body<G, FP8>(a, (blockIdx.x - seg_blocks) * 4 + (threadIdx.x >> 6), n_items, nsplit);
   }
