@@ -1042,9 +1042,13 @@ __device__ __forceinline__ void lds_tr16_k32(u32x2 (&r)[16], const uint32_t (&b)
 // Shared-segment chunks of at most this many keys stage their slot list in LDS.
 constexpr int kSegSlotCap = 2048;
 
-template <int G, bool SEG, bool FP8>
+// NW waves per block, 32 query rows each (shared-segment tiles: 4).
+template <int G, bool SEG, bool FP8, int NW = 4>
 __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item, int kvh,
                                           uint8_t (*smem)[2][MF_TILE], int32_t *slot_lds = nullptr) {
+  static_assert(NW == 4 || (NW == 8 && !SEG), "segment tiles use four waves");
+  constexpr int BM = 32 * NW;    // query rows per block
+  constexpr int RPW = 64 / NW;   // rows of each 64-key tile that one wave loads
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
@@ -1056,8 +1060,8 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     P = a.prefix_lens[b];
     const int E = a.extend_lens[b];
     nrows = E * G;
-    if (tile * MF_BM >= nrows) return;
-    const int i_last = min(E - 1, (tile * MF_BM + MF_BM - 1) / G);
+    if (tile * BM >= nrows) return;
+    const int i_last = min(E - 1, (tile * BM + BM - 1) / G);
     lo = 0;
     hi = P + i_last + 1;
     rtt_row = rtt_row_of(a, b);
@@ -1070,12 +1074,12 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     mem_off = rec[2];
     nrows = rec[3] * G;
     ks = rec[6];
-    if (tile * MF_BM >= nrows) return;
+    if (tile * BM >= nrows) return;
     rtt_row = rtt_row_of(a, rec[4]);
   }
 
   // this lane's query row
-  const int R = tile * MF_BM + wave * 32 + n;
+  const int R = tile * BM + wave * 32 + n;
   const int qi = R / G, hg = R % G;
   const bool rvalid = R < nrows;
   int64_t q_tok;
@@ -1109,8 +1113,8 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   const float sc = a.scale_log2;   // > 0
   // first query position among this wave's rows: tiles wholly at or before it need no
   // causal mask (wave-uniform)
-  const int wave_q0 = SEG ? 0x7fffffff : P + (tile * MF_BM + wave * 32) / G;
-  const bool wave_active = tile * MF_BM + wave * 32 < nrows;   // wave-uniform
+  const int wave_q0 = SEG ? 0x7fffffff : P + (tile * BM + wave * 32) / G;
+  const bool wave_active = tile * BM + wave * 32 < nrows;   // wave-uniform
 
   // loaders: wave w fills rows 16w .. 16w+15 of each tile, 4 rows per instruction;
   // lane i lands at byte 16*i of the instruction's 1 KB, i.e. row +i/16, physical chunk
@@ -1121,7 +1125,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   // bf16 tile that the matrix code below reads; the bf16 tile is single-buffered (the next
   // tile's raw bytes are in flight in the staging tile while it is used).
   constexpr int EB = FP8 ? 1 : 2;
-  constexpr int NSL = FP8 ? 2 : 4;   // slot-list entries per lane per tile
+  constexpr int NSL = FP8 ? RPW / 8 : RPW / 4;   // slot-list entries per lane per tile
   const int64_t row_bytes = static_cast<int64_t>(a.Hkv) * MF_D * EB;
   const char *kb = reinterpret_cast<const char *>(a.k_pool) + kvh * MF_D * EB;
   const char *vb = reinterpret_cast<const char *>(a.v_pool) + kvh * MF_D * EB;
@@ -1132,7 +1136,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   auto load_slots = [&](int kt) {
 #pragma unroll
     for (int j = 0; j < NSL; ++j) {
-      const int r = FP8 ? wave * 16 + 8 * j + (lane >> 3) : wave * 16 + 4 * j + (lane >> 4);
+      const int r = FP8 ? wave * RPW + 8 * j + (lane >> 3) : wave * RPW + 4 * j + (lane >> 4);
       sl[j] = rtt_row[min(kt + r, last)];
     }
   };
@@ -1145,30 +1149,30 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   // a shared-segment chunk with a single tile of rows is the only reader of its K/V
   // rows: those loads go non-temporal (agent decode step ≈ 7 % faster); chunks read by
   // several row tiles, and extend tiles, keep them in the XCD's L2 for the other tiles
-  const bool nt_rows = SEG && nrows <= MF_BM;   // block-uniform
+  const bool nt_rows = SEG && nrows <= BM;   // block-uniform
   auto issue = [&](int stage) {
 #pragma unroll
     for (int j = 0; j < NSL; ++j) {
       if constexpr (FP8) {
         const uint64_t off = row_off(sl[j], (lane & 7) * 16u);
         if (nt_rows) {
-          lds_load16<1>(kb + off, stg + (wave * 16 + 8 * j) * 128);
-          lds_load16<1>(vb + off, stg + 8192 + (wave * 16 + 8 * j) * 128);
+          lds_load16<1>(kb + off, stg + (wave * RPW + 8 * j) * 128);
+          lds_load16<1>(vb + off, stg + 8192 + (wave * RPW + 8 * j) * 128);
         } else {
-          lds_load16(kb + off, stg + (wave * 16 + 8 * j) * 128);
-          lds_load16(vb + off, stg + 8192 + (wave * 16 + 8 * j) * 128);
+          lds_load16(kb + off, stg + (wave * RPW + 8 * j) * 128);
+          lds_load16(vb + off, stg + 8192 + (wave * RPW + 8 * j) * 128);
         }
         rsc[j] = a.kv_scale[sl[j]];
       } else {
-        const int r = wave * 16 + 4 * j + (lane >> 4);
+        const int r = wave * RPW + 4 * j + (lane >> 4);
         const int c = (lane & 15) ^ mf_row_swz(r);
         const uint64_t off = row_off(sl[j], c * 16u);
         if (nt_rows) {
-          lds_load16<1>(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
-          lds_load16<1>(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
+          lds_load16<1>(kb + off, &smem[stage][0][(wave * RPW + 4 * j) * 256]);
+          lds_load16<1>(vb + off, &smem[stage][1][(wave * RPW + 4 * j) * 256]);
         } else {
-          lds_load16(kb + off, &smem[stage][0][(wave * 16 + 4 * j) * 256]);
-          lds_load16(vb + off, &smem[stage][1][(wave * 16 + 4 * j) * 256]);
+          lds_load16(kb + off, &smem[stage][0][(wave * RPW + 4 * j) * 256]);
+          lds_load16(vb + off, &smem[stage][1][(wave * RPW + 4 * j) * 256]);
         }
       }
     }
@@ -1178,7 +1182,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
     if constexpr (FP8) {
 #pragma unroll
       for (int j = 0; j < NSL; ++j) {
-        const int r = wave * 16 + 8 * j + (lane >> 3), c = lane & 7;
+        const int r = wave * RPW + 8 * j + (lane >> 3), c = lane & 7;
 #pragma unroll
         for (int kv = 0; kv < 2; ++kv) {
           const u32x4 raw = *reinterpret_cast<const u32x4 *>(stg + kv * 8192 + r * 128 + c * 16);
@@ -1383,7 +1387,7 @@ __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item,
   const int lim = min(hi - MF_BN, wave_q0 - (MF_BN - 1));
   bool ring = false;
   if constexpr (SEG && !FP8)   // (uniform) chunks of one row tile
-    ring = slot_lds != nullptr && hi - lo <= kSegSlotCap && nrows <= MF_BM;
+    ring = slot_lds != nullptr && hi - lo <= kSegSlotCap && nrows <= BM;
   if (ring) {
     // Shared-segment chunk of one row tile, bf16: its tiles wait on memory, not on the
     // matrix cores, so the chunk runs as 32-key tiles through a four-deep ring (three
@@ -1577,13 +1581,15 @@ __host__ __device__ __forceinline__ int seg_block_count(int tiles, int groups) {
 // extend: logical block -> (tile, request, kvh), tile fastest and in decreasing order:
 // a causal request's last row tiles have the most keys, and dispatching them first keeps
 // the launch from ending on its longest blocks
+// bf16 blocks are eight waves (256 query rows) sharing each K/V tile; fp8 blocks four
 template <int G, bool FP8>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
+__global__ __launch_bounds__(FP8 ? 256 : 512, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
   const int nblocks = tiles * items * a.Hkv;
   const int lb = xcd_logical(blockIdx.x, nblocks);
   if (lb >= nblocks) return;
-  mfma_body<G, false, FP8>(a, tiles - 1 - lb % tiles, (lb / tiles) % items, lb / (tiles * items), smem);
+  mfma_body<G, false, FP8, FP8 ? 4 : 8>(a, tiles - 1 - lb % tiles, (lb / tiles) % items,
+                                       lb / (tiles * items), smem);
 }
 
 // One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
@@ -1755,7 +1761,7 @@ template <int G, bool FP8>
 static hipError_t launch_mfma(const AttnArgs &a, unsigned tiles, unsigned items, hipStream_t s) {
   const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
   if (n > 0x7fffffffull) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(256);
+  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(FP8 ? 256 : 512);
   launch(attn_mfma_kernel<G, FP8>, grid, block, 0, s, a, tiles, items);
   return hipGetLastError();
 }
@@ -1808,7 +1814,8 @@ static hipError_t mfma_g(int G, const AttnArgs &a, unsigned tiles, unsigned item
 
 hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
   if (items == 0 || max_rows <= 0) return hipSuccess;
-  const unsigned tiles = static_cast<unsigned>((max_rows + MF_BM - 1) / MF_BM);
+  const int bm = fp8 ? MF_BM : 2 * MF_BM;   // query rows per extend block
+  const unsigned tiles = static_cast<unsigned>((max_rows + bm - 1) / bm);
   return fp8 ? mfma_g<true>(G, a, tiles, items, s) : mfma_g<false>(G, a, tiles, items, s);
 }
 
