@@ -1581,14 +1581,14 @@ __host__ __device__ __forceinline__ int seg_block_count(int tiles, int groups) {
 // extend: logical block -> (tile, request, kvh), tile fastest and in decreasing order:
 // a causal request's last row tiles have the most keys, and dispatching them first keeps
 // the launch from ending on its longest blocks
-// bf16 blocks are eight waves (256 query rows) sharing each K/V tile; fp8 blocks four
+// blocks of eight waves (256 query rows) sharing each K/V tile
 template <int G, bool FP8>
-__global__ __launch_bounds__(FP8 ? 256 : 512, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
+__global__ __launch_bounds__(512, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
   const int nblocks = tiles * items * a.Hkv;
   const int lb = xcd_logical(blockIdx.x, nblocks);
   if (lb >= nblocks) return;
-  mfma_body<G, false, FP8, FP8 ? 4 : 8>(a, tiles - 1 - lb % tiles, (lb / tiles) % items,
+  mfma_body<G, false, FP8, 8>(a, tiles - 1 - lb % tiles, (lb / tiles) % items,
                                        lb / (tiles * items), smem);
 }
 
@@ -1761,7 +1761,7 @@ template <int G, bool FP8>
 static hipError_t launch_mfma(const AttnArgs &a, unsigned tiles, unsigned items, hipStream_t s) {
   const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
   if (n > 0x7fffffffull) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(FP8 ? 256 : 512);
+  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(512);
   launch(attn_mfma_kernel<G, FP8>, grid, block, 0, s, a, tiles, items);
   return hipGetLastError();
 }
@@ -1814,7 +1814,7 @@ static hipError_t mfma_g(int G, const AttnArgs &a, unsigned tiles, unsigned item
 
 hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
   if (items == 0 || max_rows <= 0) return hipSuccess;
-  const int bm = fp8 ? MF_BM : 2 * MF_BM;   // query rows per extend block
+  const int bm = 2 * MF_BM;   // query rows per extend block (eight waves)
   const unsigned tiles = static_cast<unsigned>((max_rows + bm - 1) / bm);
   return fp8 ? mfma_g<true>(G, a, tiles, items, s) : mfma_g<false>(G, a, tiles, items, s);
 }
