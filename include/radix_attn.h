@@ -343,8 +343,8 @@ radix_status radix_attn_decode_workspace_size(const radix_attn_shape *shape, int
  * computed, the shared part being reused (page "49 · RadixAttention, eviction và
  * cache churn", §2). Errors: E_UNSUPPORTED (shape not compiled, or MLA), E_INVAL
  * (missing buffers, negative sizes, max_extend > total_extend); nothing is launched.
- * No workspace: each 256-row query tile (a block of eight waves) reads the whole key
- * range itself.
+ * No workspace: each query tile (128 or 256 rows, chosen from the batch's average extend
+ * length) reads the whole key range itself.
  * Request b (rows req_rows[b] of req_to_token, or b when req_rows is NULL) has
  * prefix_lens[b] cached tokens and extend_lens[b] new ones; its new tokens are
  * rows cu_extend[b] .. cu_extend[b+1]-1 of q/k_new/v_new/out. New token i sits

@@ -108,9 +108,11 @@ hipError_t mla(const MlaArgs &a, hipStream_t s);
 // 2: shared segment -> partial, 3: decode private tail -> final output (merges shared partials)
 hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, unsigned splits,
                 hipStream_t s);
-// extend attention with bf16 MFMA tiles (128 query rows x 64-key tiles); fp8: K/V bytes
+// extend attention with bf16 MFMA tiles (128 or 256 query rows, chosen per batch, x 64-key
+// tiles; total_rows = the batch's extend tokens x query heads per KV head); fp8: K/V bytes
 // times their slot's scale, rounded to bf16 as the tiles are staged
-hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s);
+hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items,
+                int64_t total_rows, hipStream_t s);
 // bf16 decode over the private keys of each request (split into `splits` chunks): output
 // written directly, or partials merged in-kernel by the last producer (merge_cnt); fp8 K/V
 // rows are converted exactly and their scale applied to the score and the probability

@@ -439,7 +439,8 @@ radix_status radix_attn_extend(const radix_attn_shape *shape, const radix_kv_buf
   const Kind kind = classify(shape);
   if (gqa_mfma(kind)) {
     Timed t(K_EXTEND_MFMA, s);
-    return hip_status(radix_launch::mfma(G, kind == Kind::GqaFp8, a, max_extend * G, batch, s),
+    return hip_status(radix_launch::mfma(G, kind == Kind::GqaFp8, a, max_extend * G, batch,
+                                         static_cast<int64_t>(total_extend) * G, s),
                       "extend launch");
   }
   Timed t(K_EXTEND_VALU, s);

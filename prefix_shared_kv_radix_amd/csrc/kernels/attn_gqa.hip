@@ -1581,15 +1581,15 @@ __host__ __device__ __forceinline__ int seg_block_count(int tiles, int groups) {
 // extend: logical block -> (tile, request, kvh), tile fastest and in decreasing order:
 // a causal request's last row tiles have the most keys, and dispatching them first keeps
 // the launch from ending on its longest blocks
-// blocks of eight waves (256 query rows) sharing each K/V tile
-template <int G, bool FP8>
-__global__ __launch_bounds__(512, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
+// NW waves (32 * NW query rows) share each K/V tile
+template <int G, bool FP8, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
   const int nblocks = tiles * items * a.Hkv;
   const int lb = xcd_logical(blockIdx.x, nblocks);
   if (lb >= nblocks) return;
-  mfma_body<G, false, FP8, 8>(a, tiles - 1 - lb % tiles, (lb / tiles) % items,
-                                       lb / (tiles * items), smem);
+  mfma_body<G, false, FP8, NW>(a, tiles - 1 - lb % tiles, (lb / tiles) % items,
+                               lb / (tiles * items), smem);
 }
 
 // One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
@@ -1757,12 +1757,14 @@ hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, u
               : valu_g<float, 64>(G, mode, a, items, splits, s);
 }
 
-template <int G, bool FP8>
-static hipError_t launch_mfma(const AttnArgs &a, unsigned tiles, unsigned items, hipStream_t s) {
+template <int G, bool FP8, int NW>
+static hipError_t launch_mfma(const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
+  const unsigned tiles = static_cast<unsigned>((max_rows + 32 * NW - 1) / (32 * NW));
   const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
   if (n > 0x7fffffffull) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(512);
-  launch(attn_mfma_kernel<G, FP8>, grid, block, 0, s, a, tiles, items);
+  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(64 * NW);
+  launch(attn_mfma_kernel<G, FP8, NW>, grid, block, 0, s, a, static_cast<int>(tiles),
+         static_cast<int>(items));
   return hipGetLastError();
 }
 
@@ -1801,22 +1803,30 @@ hipError_t decode_fused(int G, bool fp8, const AttnArgs &a, int max_rows, unsign
              : fused_g<false>(G, a, tiles, seg_items, n_items, nsplit, s);
 }
 
-template <bool FP8>
-static hipError_t mfma_g(int G, const AttnArgs &a, unsigned tiles, unsigned items, hipStream_t s) {
+template <bool FP8, int NW>
+static hipError_t mfma_g(int G, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
   switch (G) {
-    case 1: return launch_mfma<1, FP8>(a, tiles, items, s);
-    case 2: return launch_mfma<2, FP8>(a, tiles, items, s);
-    case 4: return launch_mfma<4, FP8>(a, tiles, items, s);
-    case 8: return launch_mfma<8, FP8>(a, tiles, items, s);
+    case 1: return launch_mfma<1, FP8, NW>(a, max_rows, items, s);
+    case 2: return launch_mfma<2, FP8, NW>(a, max_rows, items, s);
+    case 4: return launch_mfma<4, FP8, NW>(a, max_rows, items, s);
+    case 8: return launch_mfma<8, FP8, NW>(a, max_rows, items, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
+// Eight-wave blocks (256 query rows) halve the K/V tile traffic when requests fill them.
+// Four-wave blocks serve batches of short extends (on average under 3/4 of such a tile)
+// and batches whose longest request has more than twice the average rows: the grid is
+// sized by the longest, and blocks past a request's rows exit at once, but a 512-thread
+// block can only be placed on a CU with all its wave slots free (a re-extend batch with a
+// few long requests left 88 % of an eight-wave grid empty and ran 57 % slower).
+hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items,
+                int64_t total_rows, hipStream_t s) {
   if (items == 0 || max_rows <= 0) return hipSuccess;
-  const int bm = 2 * MF_BM;   // query rows per extend block (eight waves)
-  const unsigned tiles = static_cast<unsigned>((max_rows + bm - 1) / bm);
-  return fp8 ? mfma_g<true>(G, a, tiles, items, s) : mfma_g<false>(G, a, tiles, items, s);
+  const bool wide = total_rows >= static_cast<int64_t>(items) * (3 * 2 * MF_BM / 4) &&
+                    2 * total_rows >= static_cast<int64_t>(items) * max_rows;
+  if (fp8) return wide ? mfma_g<true, 8>(G, a, max_rows, items, s) : mfma_g<true, 4>(G, a, max_rows, items, s);
+  return wide ? mfma_g<false, 8>(G, a, max_rows, items, s) : mfma_g<false, 4>(G, a, max_rows, items, s);
 }
 
 hipError_t combine(bool bf16, const AttnArgs &a, int batch, int Dv, hipStream_t s) {
