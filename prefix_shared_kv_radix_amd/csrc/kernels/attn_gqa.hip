@@ -16,7 +16,7 @@
 //                     16-byte loads, DPP row reductions, online softmax in
 //                     registers, cross-wave merge in LDS. Used for the
 //                     private tail of decode (split-KV) and for fp32.
-//   attn_mfma_kernel  128 query rows x 64-key tiles with bf16 MFMA
+//   attn_mfma_kernel  128 or 256 query rows x 64-key tiles with bf16 MFMA
 //                     (32x32x16): S^T = K Q^T keeps a query row per lane so
 //                     the softmax is lane-local; P^T feeds O^T = V^T P^T
 //                     straight from registers. Query rows are either a
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(256, G >= 8 ? 1 : 2) void tail_bf16_kernel(AttnArgs
 
 // ------------------------------------------------------------------ MFMA kernel
 constexpr int MF_D = 128;
-constexpr int MF_BM = 128;   // query rows per block (4 waves x 32)
+constexpr int MF_BM = 128;   // query rows per four-wave block (4 waves x 32)
 constexpr int MF_BN = 64;    // keys per tile
 constexpr int MF_TILE = MF_BN * MF_D * 2;   // bytes of one K (or V) tile: 64 rows x 256 B
 
@@ -1029,7 +1029,11 @@ __device__ __forceinline__ void lds_tr16_k32(u32x2 (&r)[16], const uint32_t (&b)
       : "memory");
 }
 
-// 128 query rows (4 waves x 32) against 64-key tiles, bf16 MFMA 32x32x16.
+// Shared-segment chunks of at most this many keys stage their slot list in LDS.
+constexpr int kSegSlotCap = 2048;
+
+// 32 * NW query rows (NW waves x 32; shared-segment tiles: 4 waves) against 64-key
+// tiles, bf16 MFMA 32x32x16.
 //   S^T = K Q^T : A = K rows from LDS, B = Q in registers; a lane holds one query row
 //                 (column) and 16 keys, so the row softmax is lane-local plus one
 //                 exchange with lane ^ 32.
@@ -1039,10 +1043,6 @@ __device__ __forceinline__ void lds_tr16_k32(u32x2 (&r)[16], const uint32_t (&b)
 // K/V tiles go global -> LDS with direct 16-byte loads, two stages: tile t+1 is in flight
 // while tile t is multiplied. Query rows are a request's new tokens x heads (extend,
 // causal) or the members of a shared radix segment x heads (decode partials).
-// Shared-segment chunks of at most this many keys stage their slot list in LDS.
-constexpr int kSegSlotCap = 2048;
-
-// NW waves per block, 32 query rows each (shared-segment tiles: 4).
 template <int G, bool SEG, bool FP8, int NW = 4>
 __device__ __forceinline__ void mfma_body(const AttnArgs &a, int tile, int item, int kvh,
                                           uint8_t (*smem)[2][MF_TILE], int32_t *slot_lds = nullptr) {
