@@ -1580,8 +1580,8 @@ __host__ __device__ __forceinline__ int seg_block_count(int tiles, int groups) {
 
 // extend: logical block -> (tile, request, kvh), tile fastest and in decreasing order:
 // a causal request's last row tiles have the most keys, and dispatching them first keeps
-// the launch from ending on its longest blocks
-// NW waves (32 * NW query rows) share each K/V tile
+// the launch from ending on its longest blocks. NW waves (32 * NW query rows) share each
+// K/V tile; launched with four (the eight-wave tiles run in the persistent kernel below)
 template <int G, bool FP8, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a, int tiles, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
@@ -1590,6 +1590,36 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a, int t
   if (lb >= nblocks) return;
   mfma_body<G, false, FP8, NW>(a, tiles - 1 - lb % tiles, (lb / tiles) % items,
                                lb / (tiles * items), smem);
+}
+
+// Persistent extend with eight-wave blocks, as many as are resident at once (P per XCD).
+// The logical blocks are split into 8 contiguous ranges, one per XCD as the non-persistent
+// launch maps them; block j of an XCD walks its range in snake order (j, 2P-1-j, 2P+j,
+// 4P-1-j, ...), so that the long row tiles (late query rows see more keys) and the short
+// ones of the same requests share out evenly, and it skips row tiles past a request's end.
+template <int G, bool FP8>
+__global__ __launch_bounds__(512, 2) void attn_mfma_persist_kernel(AttnArgs a, int tiles, int items) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][MF_TILE];   // [stage][K, V]
+  const int nblocks = tiles * items * a.Hkv;
+  const int per = (nblocks + 7) / 8;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, P = gridDim.x >> 3;
+  // logical block k of this block's walk, or -1 past its end (the walk is increasing)
+  auto at = [&](int k) {
+    const int idx = (k & 1) ? (k + 1) * P - 1 - j : k * P + j;
+    const int lb = xcd * per + idx;
+    return idx < per && lb < nblocks ? lb : -1;
+  };
+  bool first = true;
+  for (int k = 0;; ++k) {
+    const int lb = at(k);
+    if (lb < 0) break;
+    const int tile = tiles - 1 - lb % tiles, item = (lb / tiles) % items;
+    if (tile * 256 >= a.extend_lens[item] * G) continue;   // block-uniform
+    // every wave is done with the previous row tile's K/V before this one's loads land
+    if (!first) lds_barrier();
+    first = false;
+    mfma_body<G, false, FP8, 8>(a, tile, item, lb / (tiles * items), smem);
+  }
 }
 
 // One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
@@ -1762,9 +1792,32 @@ static hipError_t launch_mfma(const AttnArgs &a, int max_rows, unsigned items, h
   const unsigned tiles = static_cast<unsigned>((max_rows + 32 * NW - 1) / (32 * NW));
   const uint64_t n = static_cast<uint64_t>(tiles) * items * a.Hkv;
   if (n > 0x7fffffffull) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(64 * NW);
-  launch(attn_mfma_kernel<G, FP8, NW>, grid, block, 0, s, a, static_cast<int>(tiles),
-         static_cast<int>(items));
+  if constexpr (NW == 8) {
+    // persistent: the blocks resident at once on this device (cached per device),
+    // rounded down to a multiple of the 8 XCDs
+    static std::atomic<int> resident[64];   // one table per kernel instantiation
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int fit = dev < 64 ? resident[dev].load(std::memory_order_relaxed) : 0;
+    if (fit == 0) {
+      int per_cu = 0, cus = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_persist_kernel<G, FP8>, 512, 0);
+      if (e != hipSuccess) return e;
+      e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      fit = per_cu * cus >= 8 ? per_cu * cus : 8;
+      if (dev < 64) resident[dev].store(fit, std::memory_order_relaxed);
+    }
+    const uint64_t per = (n + 7) / 8, pmax = static_cast<uint64_t>(fit / 8);
+    dim3 grid(static_cast<unsigned>(8 * (per < pmax ? per : pmax))), block(512);
+    launch(attn_mfma_persist_kernel<G, FP8>, grid, block, 0, s, a, static_cast<int>(tiles),
+           static_cast<int>(items));
+  } else {
+    dim3 grid(static_cast<unsigned>(8 * ((n + 7) / 8))), block(64 * NW);
+    launch(attn_mfma_kernel<G, FP8, NW>, grid, block, 0, s, a, static_cast<int>(tiles),
+           static_cast<int>(items));
+  }
   return hipGetLastError();
 }
 

@@ -342,6 +342,17 @@ def test_extend_batch_with_fully_cached_prompts(dtype):
     assert chk.checked > 0
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_extend_ragged_turns_many_tiles(kv):
+    """Three chat turns of 16 conversations, turn lengths 150-300 tokens (600-1200 query
+    rows per KV head): the eight-wave extend tiles, more of them than resident blocks,
+    so each block runs several row tiles in turn (and skips the empty last tiles of the
+    shorter requests); every request's first, last and sampled middle rows."""
+    from workloads import chat_tree
+    w = chat_tree(41, gqa128_shape(kv), 16, 3, 150, 300, pool_frac=1.0, q_rows=4096)
+    _run(w, Checker(w))
+
+
 @pytest.mark.parametrize("use_plan,splits", [(True, 0), (False, 1), (False, 3), (True, 2)])
 def test_few_shot_fp8_kv_small(use_plan, splits):
     """GQA-128 with fp8 E4M3 K/V (one scale per token): extend tiles and shared-segment
