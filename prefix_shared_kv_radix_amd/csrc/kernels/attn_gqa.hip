@@ -1623,8 +1623,9 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_persist_kernel(AttnArgs a, i
 }
 
 // One decode step with a plan: blocks [0, seg_blocks) are shared-segment MFMA tiles,
-// the rest are private-tail waves (4 per block); both write partials that
-// combine_kernel merges. Matrix-core work and the memory-bound tail overlap.
+// the rest are private-tail waves (4 per block); both write partials, and the last
+// producer of each (request, KV head) merges them into the output (arrival counter).
+// Matrix-core work and the memory-bound tail overlap.
 template <int G, bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_fused_kernel(AttnArgs a, int tiles, int seg_items,
                                                              int n_items, int nsplit) {
