@@ -342,14 +342,16 @@ def test_extend_batch_with_fully_cached_prompts(dtype):
     assert chk.checked > 0
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_extend_ragged_turns_many_tiles(kv):
-    """Three chat turns of 16 conversations, turn lengths 150-300 tokens (600-1200 query
-    rows per KV head): the eight-wave extend tiles, more of them than resident blocks,
-    so each block runs several row tiles in turn (and skips the empty last tiles of the
-    shorter requests); every request's first, last and sampled middle rows."""
-    from workloads import chat_tree
-    w = chat_tree(41, gqa128_shape(kv), 16, 3, 150, 300, pool_frac=1.0, q_rows=4096)
+@pytest.mark.parametrize("kv,hq,n_conv", [("bf16", 32, 16), ("fp8", 32, 16), ("bf16", 8, 40),
+                                           ("bf16", 16, 24), ("bf16", 64, 16), ("fp8", 64, 16)])
+def test_extend_ragged_turns_many_tiles(kv, hq, n_conv):
+    """Three chat turns, turn lengths 150-300 tokens, 1, 2, 4 or 8 query heads per KV
+    head: the eight-wave (256-row) extend tiles, more of them than resident blocks, so
+    each block runs two to five row tiles in turn (and skips the empty last tiles of
+    the shorter requests); every request's first, last and sampled middle rows."""
+    import dataclasses
+    shape = dataclasses.replace(gqa128_shape(kv), num_q_heads=hq)
+    w = chat_tree(41, shape, n_conv, 3, 150, 300, pool_frac=1.0, q_rows=4096)
     _run(w, Checker(w))
 
 
