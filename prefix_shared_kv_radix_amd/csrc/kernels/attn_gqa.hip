@@ -1870,10 +1870,10 @@ static hipError_t mfma_g(int G, const AttnArgs &a, int max_rows, unsigned items,
 
 // Eight-wave blocks (256 query rows) halve the K/V tile traffic when requests fill them.
 // Four-wave blocks serve batches of short extends (on average under 3/4 of such a tile)
-// and batches whose longest request has more than twice the average rows: the grid is
-// sized by the longest, and blocks past a request's rows exit at once, but a 512-thread
-// block can only be placed on a CU with all its wave slots free (a re-extend batch with a
-// few long requests left 88 % of an eight-wave grid empty and ran 57 % slower).
+// and batches whose longest request has more than twice the average rows: the eight-wave
+// tiles run as a persistent grid whose static walk cannot balance a few long requests
+// against many short ones (a re-extend batch of that kind took 4.46 ms that way against
+// 2.52 ms as a four-wave grid, which the hardware dispatcher balances).
 hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items,
                 int64_t total_rows, hipStream_t s) {
   if (items == 0 || max_rows <= 0) return hipSuccess;
