@@ -239,6 +239,52 @@ def test_decode_plan_brute_force():
                                                   adm[i][1][plan.seg_start[s]:plan.seg_end[s]])
 
 
+def test_decode_plan_request_order_groups_root_segments():
+    """Random batches (members of a prefix in any batch order): req_order is a
+    permutation of the batch that lists the members of each segment starting at the
+    root together (a request has at most one), and the requests with no shared
+    segment last, in batch order."""
+    for seed in range(40):
+        t, p, adm = _random_admissions(seed)
+        plan = t.decode_plan([a[2] for a in adm])
+        order = np.asarray(plan.req_order).tolist()
+        B = len(adm)
+        assert sorted(order) == list(range(B))
+        at = {b: i for i, b in enumerate(order)}
+        shared = set()
+        for s_ in range(plan.num_segments):
+            mem = plan.seg_members[plan.seg_member_off[s_]:plan.seg_member_off[s_ + 1]].tolist()
+            shared.update(mem)
+            if plan.seg_start[s_] == 0:
+                idx = sorted(at[b] for b in mem)
+                assert idx == list(range(idx[0], idx[0] + len(idx)))
+        rest = [b for b in order if b not in shared]
+        assert order[len(order) - len(rest):] == sorted(rest)
+
+
+def test_mla_plan_keeps_each_group_on_one_xcd():
+    """Config 5 (MLA, batch 256, groups of 32 requests sharing a 2048-token prefix): the
+    MLA decode launch gives request-order positions [x * ceil(B / 8), (x + 1) * ceil(B / 8))
+    to XCD x (one key split per request at this batch), so with the plan's req_order
+    (the members of each shared segment listed together) every group's prefix rows are
+    read through one XCD's L2."""
+    w = config(5, "bf16")
+    plans = [r.plan for r in Engine(w).run().rounds if r.plan is not None]
+    assert plans
+    for plan in plans:
+        order = np.asarray(plan.req_order)
+        B = len(order)
+        assert sorted(order.tolist()) == list(range(B))
+        at = np.empty(B, np.int64)
+        at[order] = np.arange(B)
+        per = -(-B // 8)
+        assert plan.num_segments == 8
+        for s_ in range(plan.num_segments):
+            mem = np.asarray(plan.seg_members[plan.seg_member_off[s_]:plan.seg_member_off[s_ + 1]])
+            assert len(mem) == 32
+            assert len(set((at[mem] // per).tolist())) == 1
+
+
 def test_decode_plan_key_chunks():
     """Key chunks: the segments do not depend on split_keys; segment s gets
     ceil(len / split_keys) chunks (1 when split_keys <= 0 or len <= split_keys); each
