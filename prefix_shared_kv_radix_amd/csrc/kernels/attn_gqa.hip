@@ -1788,6 +1788,20 @@ hipError_t valu(bool bf16, int G, int mode, const AttnArgs &a, unsigned items, u
               : valu_g<float, 64>(G, mode, a, items, splits, s);
 }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  int c = dev < 64 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      return 256;
+    if (dev < 64) cached[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 template <int G, bool FP8, int NW>
 static hipError_t launch_mfma(const AttnArgs &a, int max_rows, unsigned items, hipStream_t s) {
   const unsigned tiles = static_cast<unsigned>((max_rows + 32 * NW - 1) / (32 * NW));
@@ -1802,12 +1816,10 @@ static hipError_t launch_mfma(const AttnArgs &a, int max_rows, unsigned items, h
     if (e != hipSuccess) return e;
     int fit = dev < 64 ? resident[dev].load(std::memory_order_relaxed) : 0;
     if (fit == 0) {
-      int per_cu = 0, cus = 0;
+      int per_cu = 0;
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_persist_kernel<G, FP8>, 512, 0);
       if (e != hipSuccess) return e;
-      e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess) return e;
-      fit = per_cu * cus >= 8 ? per_cu * cus : 8;
+      fit = per_cu * device_cus() >= 8 ? per_cu * device_cus() : 8;
       if (dev < 64) resident[dev].store(fit, std::memory_order_relaxed);
     }
     const uint64_t per = (n + 7) / 8, pmax = static_cast<uint64_t>(fit / 8);
@@ -1868,17 +1880,23 @@ static hipError_t mfma_g(int G, const AttnArgs &a, int max_rows, unsigned items,
   return hipErrorInvalidValue;
 }
 
-// Eight-wave blocks (256 query rows) halve the K/V tile traffic when requests fill them.
-// Four-wave blocks serve batches of short extends (on average under 3/4 of such a tile)
-// and batches whose longest request has more than twice the average rows: the eight-wave
-// tiles run as a persistent grid whose static walk cannot balance a few long requests
-// against many short ones (a re-extend batch of that kind took 4.46 ms that way against
-// 2.52 ms as a four-wave grid, which the hardware dispatcher balances).
+// Eight-wave blocks (256 query rows) halve the K/V tile traffic when requests fill them;
+// they run as a persistent grid (one block per CU) that walks a static share of the row
+// tiles. Four-wave blocks (two per CU, placed by the hardware dispatcher as others end)
+// serve the batches that grid handles badly:
+//  - short extends (on average under 3/4 of a 256-row tile);
+//  - a longest request with more than twice the average rows: the static walk cannot
+//    balance a few long requests against many short ones (a re-extend batch of that kind
+//    took 4.46 ms that way against 2.52 ms as a four-wave grid);
+//  - fewer than 8 row tiles of 256 rows per CU: a walk of a few tiles per block leaves
+//    the uneven tile lengths unbalanced and each tile's prologue uncovered (chat-tree
+//    turn batches, about 5 tiles per CU: 0.216 of the matrix peak against 0.237).
 hipError_t mfma(int G, bool fp8, const AttnArgs &a, int max_rows, unsigned items,
                 int64_t total_rows, hipStream_t s) {
   if (items == 0 || max_rows <= 0) return hipSuccess;
   const bool wide = total_rows >= static_cast<int64_t>(items) * (3 * 2 * MF_BM / 4) &&
-                    2 * total_rows >= static_cast<int64_t>(items) * max_rows;
+                    2 * total_rows >= static_cast<int64_t>(items) * max_rows &&
+                    total_rows * a.Hkv >= static_cast<int64_t>(8) * (2 * MF_BM) * device_cus();
   if (fp8) return wide ? mfma_g<true, 8>(G, a, max_rows, items, s) : mfma_g<true, 4>(G, a, max_rows, items, s);
   return wide ? mfma_g<false, 8>(G, a, max_rows, items, s) : mfma_g<false, 4>(G, a, max_rows, items, s);
 }

@@ -46,10 +46,19 @@ Q_POS_MUL = 7919
 # value rounding helpers (input preparation only)
 # --------------------------------------------------------------------------
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (round to nearest even); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    """Round float32 values to bfloat16 (round to nearest even); returns uint16 bit patterns.
+    Works through the values in chunks (64-bit temporaries of a whole table would take
+    several times its size)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    fu, fo = u.reshape(-1), out.reshape(-1)
+    step = 1 << 20
+    for i in range(0, fu.size, step):
+        c = fu[i:i + step].astype(np.uint64)
+        c += 0x7FFF + ((c >> 16) & 1)
+        c >>= 16
+        fo[i:i + step] = c
+    return out
 
 
 def quantize_e4m3_rows(x: np.ndarray):
