@@ -1614,6 +1614,7 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_persist_kernel(AttnArgs a, i
     const int lb = at(k);
     if (lb < 0) break;
     const int tile = tiles - 1 - lb % tiles, item = (lb / tiles) % items;
+    // a row tile is 256 query rows (8 waves x 32); past the request's rows: skip
     if (tile * 256 >= a.extend_lens[item] * G) continue;   // block-uniform
     // every wave is done with the previous row tile's K/V before this one's loads land
     if (!first) lds_barrier();
